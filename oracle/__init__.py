@@ -1,0 +1,34 @@
+"""Plain float64 CPU oracle for exact scaled-dot-product attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+its Python binding) may import, call or link anything in this package; only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it.  It shares no code with the GPU path: it receives numpy
+arrays and returns numpy arrays.
+
+Sources (web pages on FlashAttention, cited by title and section):
+
+* "Paper Notes: FlashAttention" (bv003me.vercel.app/blog/flashattention),
+  sections "What Are We Computing?", "Tiling: Block-by-Block Softmax",
+  "Background", "Key Ideas", "Worked Example".
+* "flash attention" (muhibwaqar.com/writing/flash-attention), section
+  "build it from scratch" (the 1/sqrt(d) scale and the tiled loop).
+* The aicassindra.com transformer-math page on FlashAttention, sections
+  "Online softmax: the running-max, running-sum idea", "Rescale and
+  accumulate", "The backward pass: recompute instead of store",
+  "A tiny worked example", "Common pitfalls".
+
+Modules:
+
+* :mod:`oracle.attention` -- the definition (S, P, O, LSE) and its
+  textbook chain-rule gradients, materialising S and P.
+* :mod:`oracle.online` -- the pages' tiled online-softmax forward, kept only
+  to pin the definition (tiled == one-shot) and to replay the pages' worked
+  examples step by step.
+
+Every function here is pinned by ``tests/test_oracle*.py`` against page-printed
+values, closed forms, invariants, finite differences and a library autograd;
+no function is "parity unpinned".
+"""
+
+from . import attention, online  # noqa: F401
