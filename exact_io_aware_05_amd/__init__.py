@@ -1,0 +1,171 @@
+"""Fused exact attention for MI355X (gfx950): Python binding of ``libattn.so``.
+
+The binding only marshals arguments: every step of the forward and backward
+pass runs in the HIP kernels of the C library (``include/attn.h``).  PyTorch
+tensors serve as device memory and the current HIP stream is passed through.
+There is no fallback: if the library is missing, loading it raises.
+
+Entry points carry the C names:
+
+* :func:`attn_fwd` (q, k, v, causal, scale) -> (o, lse)
+* :func:`attn_bwd` (q, k, v, o, do, lse, causal, scale) -> (dq, dk, dv)
+* :func:`attn_bwd_workspace_bytes`, :func:`attn_status_string`
+* :func:`lib` -- the raw ``ctypes.CDLL``.
+"""
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "attn_fwd",
+    "attn_bwd",
+    "attn_bwd_workspace_bytes",
+    "attn_status_string",
+    "lib",
+    "LIB_PATH",
+    "ATTN_BF16",
+    "ATTN_FP32",
+    "AttnError",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_BF16 = 0
+ATTN_FP32 = 1
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-zero status returned by the C library."""
+
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({attn_status_string(status)})")
+
+
+def lib():
+    """Load ``libattn.so`` (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m exact_io_aware_05_amd.build` "
+            "(or __graft_entry__.build())"
+        )
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp]
+    L.attn_fwd.restype = i32
+    L.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    L.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp,
+                           ctypes.c_size_t, vp]
+    L.attn_bwd.restype = i32
+    L.attn_status_string.argtypes = [i32]
+    L.attn_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def attn_status_string(status):
+    return lib().attn_status_string(int(status)).decode()
+
+
+def attn_bwd_workspace_bytes(B, H, N, d, dtype):
+    return int(lib().attn_bwd_workspace_bytes(B, H, N, d, dtype))
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _check(tensors, shape, dtype, device):
+    for name, t in tensors:
+        if t.shape != shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name}: dtype {t.dtype} != {dtype}")
+        if t.device != device:
+            raise ValueError(f"{name}: device {t.device} != {device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous [B, H, N, d]")
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None):
+    """Fused attention forward on [B, H, N, d] GPU tensors; returns (o, lse).
+
+    ``scale`` defaults to 1/sqrt(d).  ``o`` has the dtype of ``q``; ``lse`` is
+    float32 [B, H, N].  Enqueued on the current stream.
+    """
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if not q.is_cuda:
+        raise ValueError("tensors must be on a GPU")
+    _check([("q", q), ("k", k), ("v", v)], q.shape, q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check([("out", out)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    st = lib().attn_fwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        B, H, N, d, _dtype_code(q), int(bool(causal)), float(scale), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+    return out, lse
+
+
+def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, grads=None):
+    """Attention backward by recomputation; returns (dq, dk, dv).
+
+    ``o`` and ``lse`` must come from :func:`attn_fwd` with the same
+    ``causal`` and ``scale``.  ``workspace`` (a uint8 GPU tensor of at least
+    :func:`attn_bwd_workspace_bytes` bytes) is allocated when not given.
+    """
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v), ("o", o), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    _check([("dq", dq), ("dk", dk), ("dv", dv)], q.shape, q.dtype, q.device)
+    st = lib().attn_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, code, int(bool(causal)), float(scale),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+    return dq, dk, dv

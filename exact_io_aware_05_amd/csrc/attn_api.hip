@@ -1,0 +1,100 @@
+// C ABI of the attention library: host-side validation and dispatch.
+// Every check completes before the first HIP call, so an invalid argument
+// returns a status without touching the device.
+#include <math.h>
+
+#include "../../include/attn.h"
+#include "attn_launch.h"
+
+namespace {
+
+constexpr int64_t kMax31 = 2147483647LL;
+
+int check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return ATTN_E_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (B < 1 || H < 1 || N < 1) return ATTN_E_SHAPE;
+  if (B > kMax31 || H > kMax31 || N > kMax31) return ATTN_E_SHAPE;
+  if (B * H > kMax31 / N) return ATTN_E_SHAPE;  // B*H*N rows index in 31 bits
+  if (N > kMax31 / d) return ATTN_E_SHAPE;      // offsets within a head in 31 bits
+  return ATTN_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULL: return "a required pointer is NULL";
+    case ATTN_E_SHAPE: return "invalid shape (B, H, N must be >= 1 and within size limits)";
+    case ATTN_E_UNSUPPORTED: return "unsupported head dimension (64 or 128) or dtype (bf16 or fp32)";
+    case ATTN_E_SCALE: return "scale must be finite";
+    case ATTN_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_E_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+             int64_t d, int dtype, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = B * H;
+  a.n = N;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  const hipError_t e = dtype == ATTN_BF16 ? attn::fwd_bf16(a) : attn::fwd_f32(a);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+  if (check_shape(B, H, N, d, dtype) != ATTN_OK) return 0;
+  return align256((size_t)(B * H * N) * sizeof(float));
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal,
+             float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, dtype) ||
+      ((uintptr_t)workspace & 255) != 0)
+    return ATTN_E_WORKSPACE;
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsum = (float*)workspace;
+  a.bh = B * H;
+  a.n = N;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  const hipError_t e = dtype == ATTN_BF16 ? attn::bwd_bf16(a) : attn::bwd_f32(a);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Device-side building blocks shared by the attention kernels (gfx950 only).
+//
+// Matrix-core conventions used throughout (CDNA 32x32 MFMA):
+//   v_mfma_f32_32x32x16_bf16 D = A(32x16) * B(16x32) + C(32x32).
+//   Lane l supplies row (l % 32) of A and column (l % 32) of B, each as 8
+//   bf16 values of the contraction index; both operands use the same
+//   lane/slot -> contraction-index map, so any consistent assignment of the
+//   contraction index to (lane half, slot) gives the same product.
+//   The 32x32 fp32 result lives in 16 registers per lane:
+//   register r of lane l holds row 8*(r/4) + 4*(l/32) + (r%4), column l%32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row index (within a 32x32 result tile) held by register r in lane half h.
+__device__ __forceinline__ constexpr int crow(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Position of index x (within a block of 32) in the "slot order" of the 32x32
+// result layout: the 8 rows that one lane half holds in registers 8u..8u+7
+// (rows 16u + {4h..4h+3, 8+4h..8+4h+3}) become 8 consecutive positions
+// 16u + 8h + 0..7.  It swaps bits 2 and 3 of x and is its own inverse.
+__device__ __forceinline__ constexpr int slot_pos(int x) {
+  return (x & ~0xC) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Symmetric combination of the two 32-lane halves of a wave: every lane gets
+// op(x[l % 32], x[l % 32 + 32]).  v_permlane32_swap exchanges one half of its
+// two operands, so passing x twice yields both halves in one instruction.
+__device__ __forceinline__ float half_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Round two floats to bf16 (nearest, ties to even) and pack them, low first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 b = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
+  u32x4 u;
+  u[0] = pack_bf16x2(x[0], x[1]);
+  u[1] = pack_bf16x2(x[2], x[3]);
+  u[2] = pack_bf16x2(x[4], x[5]);
+  u[3] = pack_bf16x2(x[6], x[7]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Low 16 bits of a and b packed (a low), and high 16 bits of a and b packed.
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// 16-byte global load with a predicate (zero when off).
+__device__ __forceinline__ u32x4 load16_or_zero(const uint16_t* p, bool ok) {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return ok ? *reinterpret_cast<const u32x4*>(p) : z;
+}
+
+// Workgroup order.  Workgroups are handed to the 8 XCDs of the chip round
+// robin (id % 8).  This maps the hardware id to a logical id so that each
+// XCD receives a contiguous range of logical ids (tiles of the same head
+// share one L2).  Bijective for any total.
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = pid & 7, k = pid >> 3;
+  return x * q + (x < r ? x : r) + k;
+}
+
+}  // namespace attn

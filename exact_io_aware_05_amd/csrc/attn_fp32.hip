@@ -1,0 +1,272 @@
+// Float32 attention, forward and backward, on the vector ALUs (gfx950).
+//
+// The float32 path serves inputs that must be matched to ~1e-5: everything is
+// fp32 end to end (products, sums, exponentials).  It keeps the method's
+// structure -- K/V (or Q/dO) tiles staged in LDS, an online softmax with a
+// running max and sum per query ("Tiling: Block-by-Block Softmax", Paper
+// Notes page), and a backward pass that recomputes P from the saved LSE
+// ("The backward pass: recompute instead of store", aicassindra page) -- but
+// not the matrix cores: each query (or key) row is owned by 4 adjacent lanes
+// that hold the features f with f % 4 == lane % 4, and dot products are
+// finished with two butterfly shuffles.
+//
+// Backward: dK and dV are accumulated by a key-stationary kernel and dQ by a
+// query-stationary kernel, so no floating-point atomics are needed and the
+// result is deterministic.
+#include "attn_device.h"
+#include "attn_launch.h"
+
+namespace attn {
+
+namespace {
+
+__device__ __forceinline__ float quad_sum(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  return x;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                      const float* __restrict__ V, float* __restrict__ O,
+                                                      float* __restrict__ LSE, int n, int nqb, float sl2e) {
+  constexpr int BQ = 64, BK = 64, DQ = D / 4;
+  __shared__ __attribute__((aligned(16))) float ks[BK * D];
+  __shared__ __attribute__((aligned(16))) float vs[BK * D];
+  const int tid = threadIdx.x, c = tid & 3, ql = tid >> 2;
+  const int bh = blockIdx.x / nqb, qb = blockIdx.x % nqb;
+  const int qrow = qb * BQ + ql;
+  const size_t head = (size_t)bh * n * D;
+  const float* Kh = K + head;
+  const float* Vh = V + head;
+
+  float qv[DQ], acc[DQ];
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) {
+    qv[i] = qrow < n ? Q[head + (size_t)qrow * D + 4 * i + c] : 0.f;
+    acc[i] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kend = CAUSAL ? min(n, qb * BQ + BQ) : n;
+  for (int j0 = 0; j0 < kend; j0 += BK) {
+    __syncthreads();
+    for (int idx = tid; idx < BK * D / 4; idx += 256) {
+      const int row = idx / (D / 4), c4 = idx % (D / 4), key = j0 + row;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(&ks[row * D + 4 * c4]) =
+          key < n ? *reinterpret_cast<const f32x4*>(Kh + (size_t)key * D + 4 * c4) : z;
+      *reinterpret_cast<f32x4*>(&vs[row * D + 4 * c4]) =
+          key < n ? *reinterpret_cast<const f32x4*>(Vh + (size_t)key * D + 4 * c4) : z;
+    }
+    __syncthreads();
+    float s[BK];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < BK; ++jj) {
+      float part = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) part = fmaf(qv[i], ks[jj * D + 4 * i + c], part);
+      const float x = quad_sum(part) * sl2e;
+      const int key = j0 + jj;
+      const bool dead = key >= n || (CAUSAL && key > qrow);
+      s[jj] = dead ? -INFINITY : x;
+      mx = fmaxf(mx, s[jj]);
+    }
+    // Tile 0 always holds key 0, visible to every query: m_new is finite.
+    const float m_new = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int jj = 0; jj < BK; ++jj) {
+      const float p = fast_exp2(s[jj] - m_new);
+      l += p;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) acc[i] = fmaf(p, vs[jj * D + 4 * i + c], acc[i]);
+    }
+    m = m_new;
+  }
+  if (qrow < n) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) O[head + (size_t)qrow * D + 4 * i + c] = acc[i] * inv;
+    if (c == 0) LSE[(size_t)bh * n + qrow] = (m + fast_log2(l)) * kLn2;
+  }
+}
+
+// dK, dV for a block of 64 keys; streams query tiles of 32 rows.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                         const float* __restrict__ V,
+                                                         const float* __restrict__ dO,
+                                                         const float* __restrict__ LSE,
+                                                         const float* __restrict__ Dsum, float* __restrict__ dK,
+                                                         float* __restrict__ dV, int n, int nkb, float scale,
+                                                         float sl2e) {
+  constexpr int BKEY = 64, BQ = 32, DQ = D / 4;
+  __shared__ __attribute__((aligned(16))) float qs[BQ * D];
+  __shared__ __attribute__((aligned(16))) float dos[BQ * D];
+  __shared__ float lse2[BQ];
+  __shared__ float dsm[BQ];
+  const int tid = threadIdx.x, c = tid & 3, kl = tid >> 2;
+  const int bh = blockIdx.x / nkb, kb = blockIdx.x % nkb;
+  const int key = kb * BKEY + kl;
+  const size_t head = (size_t)bh * n * D;
+  const float* Qh = Q + head;
+  const float* dOh = dO + head;
+
+  float kv[DQ], vv[DQ], dk[DQ], dv[DQ];
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) {
+    kv[i] = key < n ? K[head + (size_t)key * D + 4 * i + c] : 0.f;
+    vv[i] = key < n ? V[head + (size_t)key * D + 4 * i + c] : 0.f;
+    dk[i] = 0.f;
+    dv[i] = 0.f;
+  }
+  const int istart = CAUSAL ? (kb * BKEY / BQ) * BQ : 0;
+  for (int i0 = istart; i0 < n; i0 += BQ) {
+    __syncthreads();
+    for (int idx = tid; idx < BQ * D / 4; idx += 256) {
+      const int row = idx / (D / 4), c4 = idx % (D / 4), qi = i0 + row;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(&qs[row * D + 4 * c4]) =
+          qi < n ? *reinterpret_cast<const f32x4*>(Qh + (size_t)qi * D + 4 * c4) : z;
+      *reinterpret_cast<f32x4*>(&dos[row * D + 4 * c4]) =
+          qi < n ? *reinterpret_cast<const f32x4*>(dOh + (size_t)qi * D + 4 * c4) : z;
+    }
+    if (tid < BQ) {
+      const int qi = i0 + tid;
+      lse2[tid] = qi < n ? LSE[(size_t)bh * n + qi] * kLog2e : 0.f;
+      dsm[tid] = qi < n ? Dsum[(size_t)bh * n + qi] : 0.f;
+    }
+    __syncthreads();
+    for (int ii = 0; ii < BQ; ++ii) {
+      const int qi = i0 + ii;
+      float sp = 0.f, dpp = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        sp = fmaf(qs[ii * D + 4 * i + c], kv[i], sp);
+        dpp = fmaf(dos[ii * D + 4 * i + c], vv[i], dpp);
+      }
+      const float s = quad_sum(sp);
+      const float dp = quad_sum(dpp);
+      const bool live = key < n && qi < n && (!CAUSAL || key <= qi);
+      const float p = live ? fast_exp2(s * sl2e - lse2[ii]) : 0.f;
+      const float ds = p * (dp - dsm[ii]);
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        dv[i] = fmaf(p, dos[ii * D + 4 * i + c], dv[i]);
+        dk[i] = fmaf(ds, qs[ii * D + 4 * i + c], dk[i]);
+      }
+    }
+  }
+  if (key < n) {
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) {
+      dK[head + (size_t)key * D + 4 * i + c] = dk[i] * scale;
+      dV[head + (size_t)key * D + 4 * i + c] = dv[i];
+    }
+  }
+}
+
+// dQ for a block of 64 queries; streams key tiles of 32 rows.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                        const float* __restrict__ V,
+                                                        const float* __restrict__ dO,
+                                                        const float* __restrict__ LSE,
+                                                        const float* __restrict__ Dsum, float* __restrict__ dQ,
+                                                        int n, int nqb, float scale, float sl2e) {
+  constexpr int BQ = 64, BKEY = 32, DQ = D / 4;
+  __shared__ __attribute__((aligned(16))) float ks[BKEY * D];
+  __shared__ __attribute__((aligned(16))) float vs[BKEY * D];
+  const int tid = threadIdx.x, c = tid & 3, ql = tid >> 2;
+  const int bh = blockIdx.x / nqb, qb = blockIdx.x % nqb;
+  const int qrow = qb * BQ + ql;
+  const size_t head = (size_t)bh * n * D;
+  const float* Kh = K + head;
+  const float* Vh = V + head;
+
+  float qv[DQ], dov[DQ], dq[DQ];
+#pragma unroll
+  for (int i = 0; i < DQ; ++i) {
+    qv[i] = qrow < n ? Q[head + (size_t)qrow * D + 4 * i + c] : 0.f;
+    dov[i] = qrow < n ? dO[head + (size_t)qrow * D + 4 * i + c] : 0.f;
+    dq[i] = 0.f;
+  }
+  const float l2 = qrow < n ? LSE[(size_t)bh * n + qrow] * kLog2e : 0.f;
+  const float dsq = qrow < n ? Dsum[(size_t)bh * n + qrow] : 0.f;
+  const int kend = CAUSAL ? min(n, qb * BQ + BQ) : n;
+  for (int j0 = 0; j0 < kend; j0 += BKEY) {
+    __syncthreads();
+    for (int idx = tid; idx < BKEY * D / 4; idx += 256) {
+      const int row = idx / (D / 4), c4 = idx % (D / 4), kj = j0 + row;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(&ks[row * D + 4 * c4]) =
+          kj < n ? *reinterpret_cast<const f32x4*>(Kh + (size_t)kj * D + 4 * c4) : z;
+      *reinterpret_cast<f32x4*>(&vs[row * D + 4 * c4]) =
+          kj < n ? *reinterpret_cast<const f32x4*>(Vh + (size_t)kj * D + 4 * c4) : z;
+    }
+    __syncthreads();
+    for (int jj = 0; jj < BKEY; ++jj) {
+      const int kj = j0 + jj;
+      float sp = 0.f, dpp = 0.f;
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) {
+        sp = fmaf(qv[i], ks[jj * D + 4 * i + c], sp);
+        dpp = fmaf(dov[i], vs[jj * D + 4 * i + c], dpp);
+      }
+      const float s = quad_sum(sp);
+      const float dp = quad_sum(dpp);
+      const bool live = kj < n && qrow < n && (!CAUSAL || kj <= qrow);
+      const float p = live ? fast_exp2(s * sl2e - l2) : 0.f;
+      const float ds = p * (dp - dsq);
+#pragma unroll
+      for (int i = 0; i < DQ; ++i) dq[i] = fmaf(ds, ks[jj * D + 4 * i + c], dq[i]);
+    }
+  }
+  if (qrow < n) {
+#pragma unroll
+    for (int i = 0; i < DQ; ++i) dQ[head + (size_t)qrow * D + 4 * i + c] = dq[i] * scale;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t fwd_f32_t(const FwdArgs& a) {
+  const int nqb = (int)((a.n + 63) / 64);
+  hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqb)), dim3(256), 0, a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.n, nqb,
+                     a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t bwd_f32_t(const BwdArgs& a) {
+  const int nkb = (int)((a.n + 63) / 64);
+  hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nkb)), dim3(256), 0, a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
+                     (const float*)a.dsum, (float*)a.dk, (float*)a.dv, (int)a.n, nkb, a.scale,
+                     a.scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nqb = (int)((a.n + 63) / 64);
+  hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqb)), dim3(256), 0, a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
+                     (const float*)a.dsum, (float*)a.dq, (int)a.n, nqb, a.scale, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t fwd_f32(const FwdArgs& a) {
+  if (a.d == 64) return a.causal ? fwd_f32_t<64, true>(a) : fwd_f32_t<64, false>(a);
+  return a.causal ? fwd_f32_t<128, true>(a) : fwd_f32_t<128, false>(a);
+}
+
+hipError_t bwd_f32_main(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? bwd_f32_t<64, true>(a) : bwd_f32_t<64, false>(a);
+  return a.causal ? bwd_f32_t<128, true>(a) : bwd_f32_t<128, false>(a);
+}
+
+}  // namespace attn

@@ -1,0 +1,49 @@
+// Internal launch interface between the C ABI (attn_api.hip) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int64_t bh;  // batch * heads
+  int64_t n;
+  int64_t d;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsum;  // workspace: D_i = sum_k dO_ik O_ik, float32 [bh, n]
+  int64_t bh;
+  int64_t n;
+  int64_t d;
+  bool causal;
+  float scale;
+  hipStream_t stream;
+};
+
+hipError_t fwd_bf16(const FwdArgs& a);
+hipError_t fwd_f32(const FwdArgs& a);
+hipError_t bwd_bf16(const BwdArgs& a);
+hipError_t bwd_f32(const BwdArgs& a);
+
+}  // namespace attn

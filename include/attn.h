@@ -1,0 +1,132 @@
+/*
+ * attn.h -- C ABI of a fused, exact scaled-dot-product attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per batch b and head h, tensors of shape [B, H, N, d]):
+ *
+ *   S   = scale * Q K^T                     (N x N, never stored)
+ *   P   = softmax(S) row-wise               (N x N, never stored)
+ *   O   = P V
+ *   LSE = per query row, m + ln(l), where m is the row max of S and l the sum
+ *         of exp(S - m) over the row: the softmax statistics the backward
+ *         pass recomputes P from, P_ij = exp(S_ij - LSE_i).
+ *
+ * The three-line definition is the one in "What Are We Computing?" of the page
+ * "Paper Notes: FlashAttention"; the 1/sqrt(d) scale is the one of "build it
+ * from scratch" on the "flash attention" page (here an explicit argument);
+ * the tiled loop with a running max and running sum follows "Tiling:
+ * Block-by-Block Softmax" (Paper Notes) and "Rescale and accumulate" (the
+ * aicassindra.com FlashAttention page); saving only O and the per-row
+ * statistics and recomputing S and P in the backward pass is "Background" /
+ * "Key Ideas" (Paper Notes) and "The backward pass: recompute instead of
+ * store" (aicassindra).  The causal mask ("Common pitfalls", aicassindra)
+ * keeps key j for query i when j <= i.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense, row-major [B, H, N, d] (d innermost), in device
+ *     memory, with the element type given by `dtype`; LSE and the softmax
+ *     statistics are float32 [B, H, N].  Queries and keys have the same N.
+ *   - Supported: d in {64, 128}; N >= 1; B, H >= 1; dtype ATTN_BF16 (bf16
+ *     inputs and outputs, fp32 accumulation, outputs rounded to nearest-even)
+ *     or ATTN_FP32 (fp32 throughout).  N * d must stay below 2^31 and
+ *     B * H * N below 2^31.
+ *   - The caller allocates and owns every buffer.  The library allocates no
+ *     device memory; scratch memory the backward pass needs is passed in as
+ *     `workspace`.
+ *   - Arguments are validated on the host before any HIP call; an invalid
+ *     argument returns a negative attn_status and launches nothing.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     null stream).  No call synchronises.  ATTN_E_HIP reports a launch
+ *     failure.  NaN or Inf inputs propagate; they are not detected.
+ *   - Output buffers must not alias inputs.  Calls on different streams with
+ *     disjoint outputs may run concurrently; the library holds no state.
+ */
+#ifndef EXACT_IO_AWARE_ATTN_H
+#define EXACT_IO_AWARE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_BF16 = 0, /* bfloat16 tensors */
+  ATTN_FP32 = 1  /* float32 tensors */
+} attn_dtype;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_NULL = -1,        /* a required pointer is NULL */
+  ATTN_E_SHAPE = -2,       /* B, H or N < 1, or a size limit exceeded */
+  ATTN_E_UNSUPPORTED = -3, /* head dimension or dtype not supported */
+  ATTN_E_SCALE = -4,       /* scale is NaN or infinite */
+  ATTN_E_WORKSPACE = -5,   /* workspace missing or smaller than required */
+  ATTN_E_HIP = -6          /* a HIP launch failed */
+} attn_status;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T [masked]) V and LSE.
+ *
+ *   q, k, v : inputs [B, H, N, d] of `dtype` (read only)
+ *   o       : output [B, H, N, d] of `dtype` (written)
+ *   lse     : output float32 [B, H, N], natural-log log-sum-exp of each
+ *             scaled (and masked) score row (written)
+ *   causal  : nonzero keeps only keys j <= i for query i
+ *   scale   : multiplies Q K^T before the softmax (usually 1/sqrt(d)); any
+ *             finite value
+ *   stream  : hipStream_t to enqueue on
+ *
+ * Returns ATTN_OK or a negative attn_status.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal,
+             float scale, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for this shape (0 on an invalid
+ * shape).  The workspace holds the per-row statistic D_i = sum_k dO_ik O_ik
+ * (float32 [B, H, N]).  Its content on entry does not matter; attn_bwd
+ * overwrites it.
+ */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d,
+                                int dtype);
+
+/*
+ * Backward pass by recomputation.  Given the forward inputs, its outputs O
+ * and LSE (as produced by attn_fwd with the same causal and scale) and the
+ * output gradient dO, computes
+ *
+ *   P  = exp(scale * Q K^T - LSE)            (recomputed tile by tile)
+ *   dV = P^T dO,  dP = dO V^T,  D_i = sum_k dO_ik O_ik,
+ *   dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * The pages defer these formulas to a companion article; they are the
+ * textbook chain rule of O = softmax(scale Q K^T) V.
+ *
+ *   q, k, v, o, dout : [B, H, N, d] of `dtype` (read only)
+ *   lse              : float32 [B, H, N] from attn_fwd (read only)
+ *   dq, dk, dv       : outputs [B, H, N, d] of `dtype` (written)
+ *   causal, scale    : must equal the values given to attn_fwd
+ *   workspace        : device memory of at least
+ *                      attn_bwd_workspace_bytes(B, H, N, d, dtype) bytes,
+ *                      256-byte aligned, not shared with a concurrent call
+ *
+ * The result is deterministic (no floating-point atomics).  Returns ATTN_OK
+ * or a negative attn_status.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+             int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal,
+             float scale, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXACT_IO_AWARE_ATTN_H */

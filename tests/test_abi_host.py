@@ -1,0 +1,110 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, and rejects invalid arguments before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _lib():
+    import exact_io_aware_05_amd as E
+
+    if not os.path.exists(E.LIB_PATH):
+        pytest.skip("libattn.so not built")
+    return E, E.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    _, L = _lib()
+    raw = ctypes.CDLL(L._name)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings():
+    E, _ = _lib()
+    for st in range(-6, 1):
+        s = E.attn_status_string(st)
+        assert isinstance(s, str) and s and s != "unknown status"
+    assert E.attn_status_string(-99) == "unknown status"
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _fwd(L, ptrs=(FAKE,) * 5, B=1, H=1, N=16, d=64, dtype=0, causal=0, scale=0.125):
+    return L.attn_fwd(*ptrs, B, H, N, d, dtype, causal, scale, None)
+
+
+def test_forward_argument_validation():
+    E, L = _lib()
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert _fwd(L, ptrs=ptrs) == -1
+    assert _fwd(L, d=32) == -3
+    assert _fwd(L, d=96) == -3
+    assert _fwd(L, d=256) == -3
+    assert _fwd(L, dtype=2) == -3
+    assert _fwd(L, B=0) == -2
+    assert _fwd(L, H=-1) == -2
+    assert _fwd(L, N=0) == -2
+    assert _fwd(L, N=2**31) == -2
+    assert _fwd(L, B=2**16, H=2**16, N=2) == -2
+    assert _fwd(L, N=2**24, d=128) == -2
+    assert _fwd(L, scale=float("nan")) == -4
+    assert _fwd(L, scale=float("inf")) == -4
+
+
+def _bwd(L, ptrs=(FAKE,) * 9, B=1, H=1, N=16, d=64, dtype=0, causal=0, scale=0.125, ws=FAKE * 256, wsb=None):
+    if wsb is None:
+        wsb = L.attn_bwd_workspace_bytes(B, H, N, d, dtype)
+    return L.attn_bwd(*ptrs, B, H, N, d, dtype, causal, scale, ws, wsb, None)
+
+
+def test_backward_argument_validation():
+    E, L = _lib()
+    for i in range(9):
+        ptrs = [FAKE] * 9
+        ptrs[i] = None
+        assert _bwd(L, ptrs=ptrs) == -1
+    assert _bwd(L, d=80) == -3
+    assert _bwd(L, dtype=7) == -3
+    assert _bwd(L, N=0) == -2
+    assert _bwd(L, scale=float("-inf")) == -4
+    assert _bwd(L, ws=None) == -5
+    assert _bwd(L, wsb=L.attn_bwd_workspace_bytes(1, 1, 16, 64, 0) - 1) == -5
+    assert _bwd(L, ws=FAKE * 256 + 4) == -5  # misaligned
+
+
+def test_workspace_size():
+    E, L = _lib()
+    assert E.attn_bwd_workspace_bytes(2, 3, 100, 64, 0) >= 2 * 3 * 100 * 4
+    assert E.attn_bwd_workspace_bytes(2, 3, 100, 64, 0) % 256 == 0
+    assert E.attn_bwd_workspace_bytes(0, 3, 100, 64, 0) == 0
+    assert E.attn_bwd_workspace_bytes(1, 1, 100, 48, 0) == 0
+
+
+def test_product_path_does_not_use_the_oracle():
+    """The package and its sources never reference the oracle."""
+    pkg = os.path.join(ROOT, "exact_io_aware_05_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text, os.path.join(dirpath, f)
