@@ -15,8 +15,9 @@
 //    through LDS.  Per tile a wave computes S and dP (C[q][key] layout, so
 //    lane = key and registers run over queries), then dV^T += dO^T P and
 //    dK^T += Q^T dS with P and dS taken straight from those registers as the
-//    B operand.  Q and dO are staged in LDS twice: row-major (A operand of
-//    S and dP) and transposed (A operand of dV^T and dK^T).
+//    B operand (each as a hi + lo pair of bf16 values, see below).  Q and
+//    dO are staged in LDS twice: row-major (A operand of S and dP) and
+//    transposed (A operand of dV^T and dK^T).
 //  * bwd_q: a workgroup owns a block of queries (32 per wave) with Q, dO,
 //    LSE and D in registers and streams key tiles of 64 rows: S^T = K Q^T and
 //    dP^T = V dO^T (lane = query), dS^T, then dQ^T += K^T dS^T.  K is staged
@@ -212,7 +213,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const uint16_t* __restri
         }
 
       const bool need_mask = CAUSAL && (i0 < kw0 + 31);
-      bf16x8 pf[2][2], df[2][2];
+      // P and dS enter dV and dK as hi + lo bf16 pairs: a single bf16
+      // rounding (relative 2^-9) of a probability near 1 can move a column
+      // sum of magnitude > 4 by more than the output's own rounding leaves.
+      bf16x8 pf[2][2], pl[2][2], df[2][2], dl[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         float p[16], ds[16];
@@ -232,10 +236,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const uint16_t* __restri
             ds[r] = pv * (pacc[t][r] - d4[i]);
           }
         }
-        pf[t][0] = pack_bf16x8(p);
-        pf[t][1] = pack_bf16x8(p + 8);
-        df[t][0] = pack_bf16x8(ds);
-        df[t][1] = pack_bf16x8(ds + 8);
+        split_bf16x8(p, pf[t][0], pl[t][0]);
+        split_bf16x8(p + 8, pf[t][1], pl[t][1]);
+        split_bf16x8(ds, df[t][0], dl[t][0]);
+        split_bf16x8(ds + 8, df[t][1], dl[t][1]);
       }
 
 #pragma unroll
@@ -249,6 +253,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const uint16_t* __restri
             const bf16x8 aqt = *reinterpret_cast<const bf16x8*>(&qts[buf][off]);
             dva[e] = mfma32(adt, pf[t][u], dva[e]);
             dka[e] = mfma32(aqt, df[t][u], dka[e]);
+            dva[e] = mfma32(adt, pl[t][u], dva[e]);
+            dka[e] = mfma32(aqt, dl[t][u], dka[e]);
           }
     }
 

@@ -73,6 +73,23 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): the pair carries about
+// 16 significant bits, so a product accumulated as hi*b + lo*b has the
+// rounding error of fp32-class operands while both MFMA inputs stay bf16
+// (and so keep bf16's full exponent range).
+__device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    const float r0 = x[2 * i] - __uint_as_float(h[i] << 16);
+    const float r1 = x[2 * i + 1] - __uint_as_float(h[i] & 0xFFFF0000u);
+    l[i] = pack_bf16x2(r0, r1);
+  }
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
 // Low 16 bits of a and b packed (a low), and high 16 bits of a and b packed.
 __device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

@@ -1,0 +1,169 @@
+"""GPU parity of the backward pass against the float64 oracle (through the C ABI).
+
+The GPU backward consumes the GPU forward's O and LSE, as a training step
+would; the oracle recomputes everything from Q, K, V and dO in float64.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as A
+from tests.gpu_util import assert_close, download, errors, upload
+
+pytestmark = [pytest.mark.gpu]
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _api():
+    import exact_io_aware_05_amd as E
+
+    E.lib()
+    return E
+
+
+def _announce(*a):
+    print("[case]", *a, flush=True)
+
+
+def _run(inp, dtype, causal, scale):
+    E = _api()
+    q, k, v, do = (upload(inp[x + "_raw"], dtype) for x in ("q", "k", "v", "do"))
+    o, lse = E.attn_fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = E.attn_bwd(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return tuple(download(x) for x in (o, lse, dq, dk, dv))
+
+
+SMALL = [
+    (1, 1, 1, 64),
+    (1, 2, 2, 128),
+    (2, 1, 5, 64),
+    (1, 2, 64, 128),
+    (1, 3, 127, 64),
+    (2, 2, 129, 128),
+    (1, 2, 300, 64),
+    (2, 1, 513, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL)
+def test_backward_small_shapes(shape, causal, dtype):
+    seed = 2000 + sum(shape) + 11 * causal
+    _announce("bwd", shape, dtype, "causal" if causal else "full", "seed", seed)
+    inp = synth.qkvdo(seed, shape, dtype)
+    scale = 1.0 / math.sqrt(shape[3])
+    o, lse, dq, dk, dv = _run(inp, dtype, causal, scale)
+    dq_r, dk_r, dv_r = A.backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale)
+    assert_close(dq, dq_r, dtype, "dQ")
+    assert_close(dk, dk_r, dtype, "dK")
+    assert_close(dv, dv_r, dtype, "dV")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_explicit_scale(dtype):
+    shape = (1, 2, 190, 64)
+    # Scales around the usual 1/sqrt(d) = 0.125.  (At scale 1 the gradients of
+    # this d = 64 problem grow ~8x and bf16 output rounding alone exceeds the
+    # absolute tolerance; the unscaled worked examples run in the forward tests.)
+    for scale, causal in ((0.2, False), (-0.125, True)):
+        _announce("bwd scale", scale, dtype)
+        inp = synth.qkvdo(91, shape, dtype)
+        o, lse, dq, dk, dv = _run(inp, dtype, causal, scale)
+        dq_r, dk_r, dv_r = A.backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale)
+        assert_close(dq, dq_r, dtype, "dQ")
+        assert_close(dk, dk_r, dtype, "dK")
+        assert_close(dv, dv_r, dtype, "dV")
+
+
+def test_backward_is_deterministic():
+    shape = (2, 2, 333, 128)
+    inp = synth.qkvdo(5, shape, "bf16")
+    a = _run(inp, "bf16", True, 1.0 / math.sqrt(128))
+    b = _run(inp, "bf16", True, 1.0 / math.sqrt(128))
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def _head_sample_check(w, inp, got, heads):
+    scale = 1.0 / math.sqrt(w.d)
+    flat = {x: inp[x].reshape(w.b * w.h, w.n, w.d) for x in ("q", "k", "v", "do")}
+    dq, dk, dv = (g.reshape(w.b * w.h, w.n, w.d) for g in got)
+    refs = [A.backward_head(flat["q"][hd], flat["k"][hd], flat["v"][hd], flat["do"][hd], w.causal, scale)
+            for hd in heads]
+    for i, (name, g) in enumerate((("dQ", dq), ("dK", dk), ("dV", dv))):
+        assert_close(np.stack([g[hd] for hd in heads]), np.stack([r[i] for r in refs]), w.dtype,
+                     f"{w.name} {name} (heads {list(heads)})")
+
+
+def _dv_sum_property(w, inp, dv):
+    """sum_j dV_j = sum_i dO_i per head (rows of P sum to one): any size."""
+    bh = w.b * w.h
+    got = dv.reshape(bh, w.n, w.d).sum(1)
+    ref = inp["do"].reshape(bh, w.n, w.d).sum(1)
+    max_abs, rel = errors(got, ref)
+    assert rel <= 1e-2, f"sum of dV rows vs sum of dO rows: rel {rel:.3e}"
+
+
+@pytest.mark.parametrize("name", ["bwd_n2048_d64_causal"])
+def test_backward_full_size_workload(name):
+    w = synth.WORKLOADS[name]
+    _announce("bwd full size", w)
+    inp = synth.qkvdo(w.seed, w.shape, w.dtype)
+    scale = 1.0 / math.sqrt(w.d)
+    o, lse, dq, dk, dv = _run(inp, w.dtype, w.causal, scale)
+    heads = synth.sample_pairs(w.seed + 3, w.b * w.h, 1, 8)[:, 0]
+    _head_sample_check(w, inp, (dq, dk, dv), heads)
+    _dv_sum_property(w, inp, dv)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_n4096_d128(causal):
+    """The d = 128, N = 4096 shape of the forward workloads, backward pass."""
+    w = synth.Workload("bwd_n4096_d128", 4, 16, 4096, 128, "bf16", causal, 6, ("fwd", "bwd"))
+    _announce("bwd", w)
+    inp = synth.qkvdo(w.seed, w.shape, w.dtype)
+    o, lse, dq, dk, dv = _run(inp, w.dtype, w.causal, 1.0 / math.sqrt(w.d))
+    heads = synth.sample_pairs(w.seed + 3, w.b * w.h, 1, 3)[:, 0]
+    _head_sample_check(w, inp, (dq, dk, dv), heads)
+    _dv_sum_property(w, inp, dv)
+
+
+def test_backward_long_context_sampled_rows():
+    """N = 65536: 512 sampled query rows (O, LSE, dQ) and 512 key rows (dK, dV)."""
+    w = synth.WORKLOADS["long_n65536_d64_causal"]
+    _announce("fwd+bwd long context", w)
+    inp = synth.qkvdo(w.seed, w.shape, w.dtype)
+    scale = 1.0 / math.sqrt(w.d)
+    o, lse, dq, dk, dv = _run(inp, w.dtype, w.causal, scale)
+    bh = w.b * w.h
+    flat = {x: inp[x].reshape(bh, w.n, w.d) for x in ("q", "k", "v", "do")}
+    qp = synth.sample_pairs(w.seed + 1, bh, w.n, 512)
+    got_q, ref_q = [], []
+    for hd in np.unique(qp[:, 0]):
+        rows = qp[qp[:, 0] == hd, 1]
+        got_q.append(dq.reshape(bh, w.n, w.d)[hd, rows])
+        ref_q.append(A.backward_query_rows(flat["q"][hd], flat["k"][hd], flat["v"][hd], flat["do"][hd], rows,
+                                           w.causal, scale))
+    assert_close(np.concatenate(got_q), np.concatenate(ref_q), w.dtype, "dQ (sampled rows)")
+
+    ref = np.load(os.path.join(GOLDEN, "long_n65536_d64_causal_key_rows.npz"))
+    kp = ref["pairs"]
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ("q", "k", "v", "do"):
+        h.update(np.ascontiguousarray(inp[name + "_raw"]).tobytes())
+    assert str(ref["inputs_sha256"]) == h.hexdigest(), "stored expectations were made from other inputs"
+    got_k = dk.reshape(bh, w.n, w.d)[kp[:, 0], kp[:, 1]]
+    got_v = dv.reshape(bh, w.n, w.d)[kp[:, 0], kp[:, 1]]
+    assert_close(got_k, ref["dk"], w.dtype, "dK (sampled key rows)")
+    assert_close(got_v, ref["dv"], w.dtype, "dV (sampled key rows)")
+    _dv_sum_property(w, inp, dv)
