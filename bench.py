@@ -1,0 +1,346 @@
+"""Throughput of the fused attention path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic bf16
+inputs at B=4, H=16, N=4096, d=128 (the d = 128, N >= 4096 shape the
+performance target is stated for): for the full mask and for the causal mask,
+the forward kernel (O, LSE), then the backward phases D = rowsum(dO * O),
+dK/dV and dQ.  Inputs are resident in HBM before the timed region starts.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --sweep           (one JSON line per N, d, mask, pass)
+       python bench.py --profile-pass    (one step plus a plain copy of known
+                                          size, for hardware-counter runs)
+
+Prints one JSON line.  FLOP convention: forward 4*B*H*N^2*d (two N x N x d
+products), halved under the causal mask; backward 2.5x forward (five
+products, one of them the recomputation of Q K^T).  Peak: MI355X dense bf16
+matrix throughput, 2516.6 TFLOP/s (256 CUs x 2.4 GHz x 4096 flop/clk/CU).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd/bwd TFLOP/s at N=1K–64K, d=64/128; % of bf16 MFMA peak"
+KERNEL_SOURCES = {
+    "fwd": "exact_io_aware_05_amd/csrc/attn_fwd_bf16.hip",
+    "dkdv": "exact_io_aware_05_amd/csrc/attn_bwd_bf16.hip",
+    "dq": "exact_io_aware_05_amd/csrc/attn_bwd_bf16.hip",
+    "dsum": "exact_io_aware_05_amd/csrc/attn_bwd_pre.hip",
+}
+KERNEL_NAMES = {  # substrings of the compiled kernel symbols, as rocprofv3 lists them
+    "fwd": "fwd_bf16_kernel",
+    "dkdv": "bwd_kv_kernel",
+    "dq": "bwd_q_kernel",
+    "dsum": "dsum_kernel",
+}
+
+
+def fwd_flops(bh, n, d, causal):
+    f = 4.0 * bh * n * n * d
+    return f / 2 if causal else f
+
+
+def phase_flops(phase, bh, n, d, causal):
+    """Algorithmic flops of one launch of a phase (sums to fwd + 2.5 fwd)."""
+    g = 2.0 * bh * n * n * d / (2 if causal else 1)  # one N x N x d product
+    return {"fwd": 2 * g, "dkdv": 4 * g, "dq": 1 * g, "dsum": 0.0}[phase]
+
+
+def phase_bytes(phase, bh, n, d):
+    """Minimum HBM bytes of one launch of a phase (bf16 tensors, fp32 rows)."""
+    t = 2.0 * bh * n * d  # one bf16 [B,H,N,d] tensor
+    r = 4.0 * bh * n  # one fp32 [B,H,N] vector
+    return {
+        "fwd": 4 * t + r,  # read Q, K, V; write O, LSE
+        "dsum": 2 * t + r,  # read O, dO; write D
+        "dkdv": 6 * t + 2 * r,  # read Q, K, V, dO, LSE, D; write dK, dV
+        "dq": 5 * t + 2 * r,  # read Q, K, V, dO, LSE, D; write dQ
+    }[phase]
+
+
+def source_hash(phase):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[phase]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(phase, workload, masks):
+    """HBM bytes per launch from committed counter summaries, if still current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        entry = data[workload][phase + ("_causal" if masks else "")]
+        if entry.get("source_sha256_16") != source_hash(phase):
+            return None
+        return entry["bytes_per_launch"]
+    except (KeyError, ValueError, TypeError):
+        return None
+
+
+def cpu_baseline(shape, budget_s=12.0, max_heads=256):
+    """The float64 oracle on a bounded sample of the same workload (host cores)."""
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import attention as A
+
+    b, h, n, d = shape
+    inp = synth.qkvdo(3, (1, 2, n, d), "bf16")  # two heads of the same shape and distribution
+    scale = 1.0 / math.sqrt(d)
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    while heads < max_heads and (time.perf_counter() - t0) < budget_s:
+        causal = heads % 2 == 1
+        hd = heads % 2
+        q, k, v, do = (inp[x][0, hd] for x in ("q", "k", "v", "do"))
+        A.forward_head(q, k, v, causal, scale)
+        A.backward_head(q, k, v, do, causal, scale)
+        flops += 3.5 * fwd_flops(1, n, d, causal)
+        heads += 1
+    dt = time.perf_counter() - t0
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{heads} (batch, head) slices of N={n} d={d}, alternating full/causal mask, "
+        f"forward + backward in float64 ({dt:.1f} s, {flops / 1e9:.0f} GFLOP by the same convention)",
+    }
+
+
+class Buffers:
+    def __init__(self, torch, shape, causal, seed=3):
+        import synth
+
+        inp = synth.qkvdo(seed, shape, "bf16")
+        dev = "cuda"
+
+        def up(raw):
+            return torch.from_numpy(raw.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.q, self.k, self.v, self.do = (up(inp[x + "_raw"]) for x in ("q", "k", "v", "do"))
+        b, h, n, d = shape
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((b, h, n), dtype=torch.float32, device=dev)
+        self.dsum = torch.empty((b, h, n), dtype=torch.float32, device=dev)
+        self.dq = torch.empty_like(self.q)
+        self.dk = torch.empty_like(self.k)
+        self.dv = torch.empty_like(self.v)
+        self.causal = causal
+        self.scale = 1.0 / math.sqrt(d)
+
+
+def run_step(E, bufs, events=None):
+    """One step: for each mask, forward then the three backward phases."""
+    k = 0
+    for B in bufs:
+        if events is not None:
+            events[k].record()
+        E.attn_fwd(B.q, B.k, B.v, B.causal, B.scale, out=B.o, lse=B.lse)
+        if events is not None:
+            events[k + 1].record()
+        E.attn_bwd_dsum(B.o, B.do, B.dsum)
+        if events is not None:
+            events[k + 2].record()
+        E.attn_bwd_dkdv(B.q, B.k, B.v, B.do, B.lse, B.dsum, B.causal, B.scale, dk=B.dk, dv=B.dv)
+        if events is not None:
+            events[k + 3].record()
+        E.attn_bwd_dq(B.q, B.k, B.v, B.do, B.lse, B.dsum, B.causal, B.scale, dq=B.dq)
+        if events is not None:
+            events[k + 4].record()
+        k += 5
+
+
+PHASES = ["fwd", "dsum", "dkdv", "dq"]
+
+
+def measure(torch, E, shape, steps, warmup):
+    bufs = [Buffers(torch, shape, False), Buffers(torch, shape, True)]
+    for _ in range(warmup):
+        run_step(E, bufs)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        run_step(E, bufs, ev[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    per = {}
+    for mi, mask in enumerate(("full", "causal")):
+        for pi, ph in enumerate(PHASES):
+            a = 5 * mi + pi
+            ms = [ev[s][a].elapsed_time(ev[s][a + 1]) for s in range(steps)]
+            per[(mask, ph)] = float(np.mean(ms))
+    return (t1 - t0) * 1e3 / steps, per
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(
+            f"bench.py: --gpus {args.gpus} requested; this build runs on one GPU only "
+            "(the kernels work on one device's share and there is no multi-GPU path)",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_05_amd as E
+
+    E.lib()
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+
+    if args.profile_pass:
+        shape = (4, 16, 4096, 128)
+        bufs = [Buffers(torch, shape, False), Buffers(torch, shape, True)]
+        run_step(E, bufs)
+        torch.cuda.synchronize()
+        src = torch.empty(256 * 2**20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # plain copy of 256 MiB: 256 MiB read + 256 MiB written
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": "done", "copy_bytes_each_way": 256 * 2**20}), flush=True)
+        return
+
+    if args.sweep:
+        sweep(torch, E, args.steps, args.warmup)
+        return
+
+    shape = (4, 16, 4096, 128)
+    b, h, n, d = shape
+    bh = b * h
+    ms_step, per = measure(torch, E, shape, args.steps, args.warmup)
+    total_flops = sum(3.5 * fwd_flops(bh, n, d, c) for c in (False, True))
+    value = total_flops / (ms_step * 1e-3) / 1e12
+
+    breakdown = {}
+    for mask in ("full", "causal"):
+        causal = mask == "causal"
+        fwd_ms = per[(mask, "fwd")]
+        bwd_ms = per[(mask, "dsum")] + per[(mask, "dkdv")] + per[(mask, "dq")]
+        ff = fwd_flops(bh, n, d, causal)
+        breakdown[mask] = {
+            "fwd_ms": round(fwd_ms, 4),
+            "fwd_tflops": round(ff / fwd_ms / 1e9, 1),
+            "fwd_frac_peak": round(ff / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "bwd_ms": round(bwd_ms, 4),
+            "bwd_tflops": round(2.5 * ff / bwd_ms / 1e9, 1),
+            "bwd_frac_peak": round(2.5 * ff / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "kernel_ms": {ph: round(per[(mask, ph)], 4) for ph in PHASES},
+        }
+
+    # Dominant kernel: the single launch with the largest average duration.
+    (dmask, dph), dms = max(per.items(), key=lambda kv: kv[1])
+    causal = dmask == "causal"
+    fl = phase_flops(dph, bh, n, d, causal)
+    achieved = fl / (dms * 1e-3) / 1e12
+    traffic = load_traffic(dph, "n4096_d128", causal)
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved, 1),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+        "kernel": KERNEL_NAMES[dph] + (" (causal)" if causal else " (full mask)"),
+        "kernel_ms": round(dms, 4),
+        "algorithmic_flops_per_launch": fl,
+        "min_hbm_bytes_per_launch": phase_bytes(dph, bh, n, d),
+    }
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "fused attention forward + backward, B=4 H=16 N=4096 d=128, full and causal mask",
+            "B": b,
+            "H": h,
+            "N": n,
+            "d": d,
+            "masks": ["full", "causal"],
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": roofline,
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(shape)
+    print(json.dumps(out), flush=True)
+
+
+def sweep(torch, E, steps, warmup):
+    """N in 1K..64K, d in {64, 128}, both masks: forward and backward TFLOP/s."""
+    tokens = 16384
+    for d in (64, 128):
+        hh = 2048 // d
+        for n in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
+            b = max(1, tokens // n)
+            shape = (b, hh, n, d)
+            bh = b * hh
+            ms_step, per = measure(torch, E, shape, steps, warmup)
+            for mask in ("full", "causal"):
+                causal = mask == "causal"
+                ff = fwd_flops(bh, n, d, causal)
+                fwd_ms = per[(mask, "fwd")]
+                bwd_ms = per[(mask, "dsum")] + per[(mask, "dkdv")] + per[(mask, "dq")]
+                print(
+                    json.dumps(
+                        {
+                            "B": b, "H": hh, "N": n, "d": d, "mask": mask,
+                            "fwd_ms": round(fwd_ms, 4),
+                            "fwd_tflops": round(ff / fwd_ms / 1e9, 1),
+                            "fwd_frac_peak": round(ff / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                            "bwd_ms": round(bwd_ms, 4),
+                            "bwd_tflops": round(2.5 * ff / bwd_ms / 1e9, 1),
+                            "bwd_frac_peak": round(2.5 * ff / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+                            "kernel_ms": {ph: round(per[(mask, ph)], 4) for ph in PHASES},
+                        }
+                    ),
+                    flush=True,
+                )
+            torch.cuda.empty_cache()
+
+
+if __name__ == "__main__":
+    main()

@@ -9,6 +9,8 @@ Entry points carry the C names:
 
 * :func:`attn_fwd` (q, k, v, causal, scale) -> (o, lse)
 * :func:`attn_bwd` (q, k, v, o, do, lse, causal, scale) -> (dq, dk, dv)
+* :func:`attn_bwd_dsum`, :func:`attn_bwd_dkdv`, :func:`attn_bwd_dq` -- the
+  three phases of the backward pass, for use on separate streams or timing
 * :func:`attn_bwd_workspace_bytes`, :func:`attn_status_string`
 * :func:`lib` -- the raw ``ctypes.CDLL``.
 """
@@ -20,6 +22,9 @@ import os
 __all__ = [
     "attn_fwd",
     "attn_bwd",
+    "attn_bwd_dsum",
+    "attn_bwd_dkdv",
+    "attn_bwd_dq",
     "attn_bwd_workspace_bytes",
     "attn_status_string",
     "lib",
@@ -64,6 +69,12 @@ def lib():
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp,
                            ctypes.c_size_t, vp]
     L.attn_bwd.restype = i32
+    L.attn_bwd_dsum.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, vp]
+    L.attn_bwd_dsum.restype = i32
+    L.attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp]
+    L.attn_bwd_dkdv.restype = i32
+    L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp]
+    L.attn_bwd_dq.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -169,3 +180,57 @@ def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, grad
     if st != 0:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+def attn_bwd_dsum(o, do, dsum=None):
+    """D_i = sum_k dO_ik O_ik into a float32 [B, H, N] tensor (returned)."""
+    torch = _torch()
+    B, H, N, d = o.shape
+    _check([("o", o), ("do", do)], o.shape, o.dtype, o.device)
+    if dsum is None:
+        dsum = torch.empty((B, H, N), dtype=torch.float32, device=o.device)
+    _check([("dsum", dsum)], (B, H, N), torch.float32, o.device)
+    st = lib().attn_bwd_dsum(o.data_ptr(), do.data_ptr(), dsum.data_ptr(), B, H, N, d, _dtype_code(o),
+                             _stream_ptr(o.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_dsum")
+    return dsum
+
+
+def attn_bwd_dkdv(q, k, v, do, lse, dsum, causal=False, scale=None, dk=None, dv=None):
+    """dK and dV from the recomputed probabilities; returns (dk, dv)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse), ("dsum", dsum)], (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check([("dk", dk), ("dv", dv)], q.shape, q.dtype, q.device)
+    st = lib().attn_bwd_dkdv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), dsum.data_ptr(), dk.data_ptr(),
+        dv.data_ptr(), B, H, N, d, _dtype_code(q), int(bool(causal)), float(scale), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_bwd_dkdv")
+    return dk, dv
+
+
+def attn_bwd_dq(q, k, v, do, lse, dsum, causal=False, scale=None, dq=None):
+    """dQ from the recomputed probabilities; returns dq."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse), ("dsum", dsum)], (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check([("dq", dq)], q.shape, q.dtype, q.device)
+    st = lib().attn_bwd_dq(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), dsum.data_ptr(), dq.data_ptr(),
+        B, H, N, d, _dtype_code(q), int(bool(causal)), float(scale), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_bwd_dq")
+    return dq

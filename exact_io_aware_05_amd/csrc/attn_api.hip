@@ -22,6 +22,29 @@ int check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+attn::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, float* dsum, int64_t B, int64_t H, int64_t N,
+                       int64_t d, int causal, float scale, void* stream) {
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dsum = dsum;
+  a.bh = B * H;
+  a.n = N;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -66,6 +89,42 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int 
   return align256((size_t)(B * H * N) * sizeof(float));
 }
 
+int attn_bwd_dsum(const void* o, const void* dout, float* dsum, int64_t B, int64_t H, int64_t N, int64_t d,
+                  int dtype, void* stream) {
+  if (!o || !dout || !dsum) return ATTN_E_NULL;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  attn::BwdArgs a = make_bwd(nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr, dsum, B, H,
+                             N, d, 0, 1.0f, stream);
+  return attn::bwd_dsum(a, dtype == ATTN_BF16) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse, const float* dsum,
+                  void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal, float scale,
+                  void* stream) {
+  if (!q || !k || !v || !dout || !lse || !dsum || !dk || !dv) return ATTN_E_NULL;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  attn::BwdArgs a = make_bwd(q, k, v, nullptr, dout, lse, nullptr, dk, dv, (float*)dsum, B, H, N, d, causal,
+                             scale, stream);
+  const hipError_t e = dtype == ATTN_BF16 ? attn::bwd_bf16_dkdv(a) : attn::bwd_f32_dkdv(a);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse, const float* dsum,
+                void* dq, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal, float scale,
+                void* stream) {
+  if (!q || !k || !v || !dout || !lse || !dsum || !dq) return ATTN_E_NULL;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  attn::BwdArgs a = make_bwd(q, k, v, nullptr, dout, lse, dq, nullptr, nullptr, (float*)dsum, B, H, N, d, causal,
+                             scale, stream);
+  const hipError_t e = dtype == ATTN_BF16 ? attn::bwd_bf16_dq(a) : attn::bwd_f32_dq(a);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal,
              float scale, void* workspace, size_t workspace_bytes, void* stream) {
@@ -76,25 +135,13 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, dtype) ||
       ((uintptr_t)workspace & 255) != 0)
     return ATTN_E_WORKSPACE;
-  attn::BwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.dsum = (float*)workspace;
-  a.bh = B * H;
-  a.n = N;
-  a.d = d;
-  a.causal = causal != 0;
-  a.scale = scale;
-  a.stream = (hipStream_t)stream;
-  const hipError_t e = dtype == ATTN_BF16 ? attn::bwd_bf16(a) : attn::bwd_f32(a);
-  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+  attn::BwdArgs a =
+      make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
+  const bool bf16 = dtype == ATTN_BF16;
+  if (attn::bwd_dsum(a, bf16) != hipSuccess) return ATTN_E_HIP;
+  if ((bf16 ? attn::bwd_bf16_dkdv(a) : attn::bwd_f32_dkdv(a)) != hipSuccess) return ATTN_E_HIP;
+  if ((bf16 ? attn::bwd_bf16_dq(a) : attn::bwd_f32_dq(a)) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
 }
 
 }  // extern "C"

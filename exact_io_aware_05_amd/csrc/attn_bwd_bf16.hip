@@ -422,34 +422,38 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd(const BwdArgs& a) {
+hipError_t launch_dkdv(const BwdArgs& a) {
   const int n = (int)a.n;
-  const float sl2e = a.scale * kLog2e;
-  {
-    const int nkb = (n + 127) / 128;
-    const int total = (int)(a.bh * nkb);
-    hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
-                       (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, sl2e);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    constexpr int NW = D == 128 ? 8 : 4;
-    const int nqb = (n + NW * 32 - 1) / (NW * 32);
-    const int total = (int)(a.bh * nqb);
-    hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL>), dim3(total), dim3(NW * 64), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                       a.lse, a.dsum, (uint16_t*)a.dq, n, nqb, total, a.scale, sl2e);
-  }
+  const int nkb = (n + 127) / 128;
+  const int total = (int)(a.bh * nkb);
+  hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL>), dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq(const BwdArgs& a) {
+  constexpr int NW = D == 128 ? 8 : 4;
+  const int n = (int)a.n;
+  const int nqb = (n + NW * 32 - 1) / (NW * 32);
+  const int total = (int)(a.bh * nqb);
+  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL>), dim3(total), dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
+                     (uint16_t*)a.dq, n, nqb, total, a.scale, a.scale * kLog2e);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t bwd_bf16_main(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_bwd<64, true>(a) : launch_bwd<64, false>(a);
-  return a.causal ? launch_bwd<128, true>(a) : launch_bwd<128, false>(a);
+hipError_t bwd_bf16_dkdv(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_dkdv<64, true>(a) : launch_dkdv<64, false>(a);
+  return a.causal ? launch_dkdv<128, true>(a) : launch_dkdv<128, false>(a);
+}
+
+hipError_t bwd_bf16_dq(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_dq<64, true>(a) : launch_dq<64, false>(a);
+  return a.causal ? launch_dq<128, true>(a) : launch_dq<128, false>(a);
 }
 
 }  // namespace attn

@@ -68,19 +68,4 @@ hipError_t bwd_dsum(const BwdArgs& a, bool bf16) {
   return a.d == 64 ? dsum_t<64, float>(a) : dsum_t<128, float>(a);
 }
 
-hipError_t bwd_f32_main(const BwdArgs& a);
-hipError_t bwd_bf16_main(const BwdArgs& a);
-
-hipError_t bwd_f32(const BwdArgs& a) {
-  hipError_t e = bwd_dsum(a, false);
-  if (e != hipSuccess) return e;
-  return bwd_f32_main(a);
-}
-
-hipError_t bwd_bf16(const BwdArgs& a) {
-  hipError_t e = bwd_dsum(a, true);
-  if (e != hipSuccess) return e;
-  return bwd_bf16_main(a);
-}
-
 }  // namespace attn

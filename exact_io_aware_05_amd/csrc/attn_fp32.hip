@@ -242,14 +242,17 @@ hipError_t fwd_f32_t(const FwdArgs& a) {
 }
 
 template <int D, bool CAUSAL>
-hipError_t bwd_f32_t(const BwdArgs& a) {
+hipError_t dkdv_f32_t(const BwdArgs& a) {
   const int nkb = (int)((a.n + 63) / 64);
   hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nkb)), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
                      (const float*)a.dsum, (float*)a.dk, (float*)a.dv, (int)a.n, nkb, a.scale,
                      a.scale * kLog2e);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t dq_f32_t(const BwdArgs& a) {
   const int nqb = (int)((a.n + 63) / 64);
   hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqb)), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
@@ -264,9 +267,14 @@ hipError_t fwd_f32(const FwdArgs& a) {
   return a.causal ? fwd_f32_t<128, true>(a) : fwd_f32_t<128, false>(a);
 }
 
-hipError_t bwd_f32_main(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? bwd_f32_t<64, true>(a) : bwd_f32_t<64, false>(a);
-  return a.causal ? bwd_f32_t<128, true>(a) : bwd_f32_t<128, false>(a);
+hipError_t bwd_f32_dkdv(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? dkdv_f32_t<64, true>(a) : dkdv_f32_t<64, false>(a);
+  return a.causal ? dkdv_f32_t<128, true>(a) : dkdv_f32_t<128, false>(a);
+}
+
+hipError_t bwd_f32_dq(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? dq_f32_t<64, true>(a) : dq_f32_t<64, false>(a);
+  return a.causal ? dq_f32_t<128, true>(a) : dq_f32_t<128, false>(a);
 }
 
 }  // namespace attn

@@ -43,7 +43,12 @@ struct BwdArgs {
 
 hipError_t fwd_bf16(const FwdArgs& a);
 hipError_t fwd_f32(const FwdArgs& a);
-hipError_t bwd_bf16(const BwdArgs& a);
-hipError_t bwd_f32(const BwdArgs& a);
+// Backward phases; `o` is read only by bwd_dsum, `dq` written only by the
+// *_dq launchers, `dk`/`dv` only by the *_dkdv launchers.
+hipError_t bwd_dsum(const BwdArgs& a, bool bf16);
+hipError_t bwd_bf16_dkdv(const BwdArgs& a);
+hipError_t bwd_bf16_dq(const BwdArgs& a);
+hipError_t bwd_f32_dkdv(const BwdArgs& a);
+hipError_t bwd_f32_dq(const BwdArgs& a);
 
 }  // namespace attn

@@ -122,6 +122,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              float scale, void* workspace, size_t workspace_bytes,
              void* stream);
 
+/*
+ * The backward pass in its three phases.  attn_bwd runs them in this order on
+ * one stream; they are exposed so that the two gradient phases, which are
+ * independent once D is known, can run on two streams, and so that each
+ * phase can be timed on its own.  Arguments mean what they mean for attn_bwd;
+ * `dsum` is float32 [B, H, N] device memory (D_i = sum_k dO_ik O_ik), written
+ * by attn_bwd_dsum and read by the other two.  Same validation and error
+ * behaviour as attn_bwd (a NULL dsum is ATTN_E_NULL).
+ */
+int attn_bwd_dsum(const void* o, const void* dout, float* dsum, int64_t B,
+                  int64_t H, int64_t N, int64_t d, int dtype, void* stream);
+
+int attn_bwd_dkdv(const void* q, const void* k, const void* v,
+                  const void* dout, const float* lse, const float* dsum,
+                  void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                  int64_t d, int dtype, int causal, float scale, void* stream);
+
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                const float* lse, const float* dsum, void* dq, int64_t B,
+                int64_t H, int64_t N, int64_t d, int dtype, int causal,
+                float scale, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);
 

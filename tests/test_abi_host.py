@@ -26,7 +26,15 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd", "attn_status_string"]
+    assert declared_functions() == [
+        "attn_bwd",
+        "attn_bwd_dkdv",
+        "attn_bwd_dq",
+        "attn_bwd_dsum",
+        "attn_bwd_workspace_bytes",
+        "attn_fwd",
+        "attn_status_string",
+    ]
 
 
 def test_library_exports_every_declared_symbol():
@@ -90,6 +98,25 @@ def test_backward_argument_validation():
     assert _bwd(L, ws=None) == -5
     assert _bwd(L, wsb=L.attn_bwd_workspace_bytes(1, 1, 16, 64, 0) - 1) == -5
     assert _bwd(L, ws=FAKE * 256 + 4) == -5  # misaligned
+
+
+def test_backward_phase_validation():
+    E, L = _lib()
+    assert L.attn_bwd_dsum(None, FAKE, FAKE, 1, 1, 16, 64, 0, None) == -1
+    assert L.attn_bwd_dsum(FAKE, FAKE, FAKE, 1, 1, 16, 48, 0, None) == -3
+    assert L.attn_bwd_dsum(FAKE, FAKE, FAKE, 1, 0, 16, 64, 0, None) == -2
+    for i in range(8):
+        ptrs = [FAKE] * 8
+        ptrs[i] = None
+        assert L.attn_bwd_dkdv(*ptrs, 1, 1, 16, 64, 0, 0, 0.1, None) == -1
+    assert L.attn_bwd_dkdv(*([FAKE] * 8), 1, 1, 16, 64, 3, 0, 0.1, None) == -3
+    assert L.attn_bwd_dkdv(*([FAKE] * 8), 1, 1, 16, 64, 0, 0, float("nan"), None) == -4
+    for i in range(7):
+        ptrs = [FAKE] * 7
+        ptrs[i] = None
+        assert L.attn_bwd_dq(*ptrs, 1, 1, 16, 64, 0, 1, 0.1, None) == -1
+    assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 0, 64, 0, 1, 0.1, None) == -2
+    assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 16, 64, 0, 1, float("inf"), None) == -4
 
 
 def test_workspace_size():
