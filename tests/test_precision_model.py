@@ -1,0 +1,47 @@
+"""CPU model of the backward kernels' rounding, justifying the hi + lo split.
+
+The bf16 backward rounds the probabilities P (and dS) to bf16 before they
+enter the dV (and dK) matrix products.  This test models exactly that
+arithmetic in float64 around the oracle's exact values: with a single bf16
+rounding of P, the largest dV error of a ragged causal case exceeds the 2e-2
+tolerance (the GPU measured the same 0.0203); with P = hi + lo (two bf16
+values) the error falls to the output-rounding floor.
+"""
+
+import math
+
+import numpy as np
+import torch
+
+import synth
+from oracle import attention as A
+
+
+def _bf16(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).double().numpy()
+
+
+def _hilo(x):
+    hi = _bf16(x)
+    return hi + _bf16(x - hi)
+
+
+def test_single_bf16_probabilities_exceed_tolerance_and_hilo_does_not():
+    shape, causal = (2, 2, 129, 128), True
+    seed = 2000 + sum(shape) + 11
+    inp = synth.qkvdo(seed, shape, "bf16")
+    scale = 1.0 / math.sqrt(shape[3])
+    q, k, do = inp["q"], inp["k"], inp["do"]
+    _, lse = A.forward(q, k, inp["v"], causal, scale)
+    _, _, dv_ref = A.backward(q, k, inp["v"], do, causal, scale)
+    err_bf16, err_hilo, err_floor = 0.0, 0.0, 0.0
+    for b in range(shape[0]):
+        for h in range(shape[1]):
+            p = np.exp(A.scores(q[b, h], k[b, h], scale, causal) - lse[b, h][:, None])
+            ref = dv_ref[b, h]
+            err_bf16 = max(err_bf16, np.abs(_bf16(_bf16(p).T @ do[b, h]) - ref).max())
+            err_hilo = max(err_hilo, np.abs(_bf16(_hilo(p).T @ do[b, h]) - ref).max())
+            err_floor = max(err_floor, np.abs(_bf16(ref) - ref).max())
+    assert err_bf16 > 2e-2
+    assert err_hilo < 1.2 * err_floor + 1e-3
+    assert err_hilo < 1.5e-2
