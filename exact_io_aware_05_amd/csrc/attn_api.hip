@@ -16,7 +16,8 @@ int check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
   if (B < 1 || H < 1 || N < 1) return ATTN_E_SHAPE;
   if (B > kMax31 || H > kMax31 || N > kMax31) return ATTN_E_SHAPE;
   if (B * H > kMax31 / N) return ATTN_E_SHAPE;  // B*H*N rows index in 31 bits
-  if (N > kMax31 / d) return ATTN_E_SHAPE;      // offsets within a head in 31 bits
+  if (N > (1LL << 30) / d) return ATTN_E_SHAPE;  // N*d <= 2^30: byte offsets in a head, plus a
+                                                  // tile of padding rows, fit 32 bits
   return ATTN_OK;
 }
 

@@ -12,19 +12,22 @@
 // Two kernels, neither uses atomics (deterministic results):
 //  * bwd_kv: a workgroup owns 128 keys (32 per wave) and keeps K, V and the
 //    dK, dV accumulators in registers while query tiles of 64 rows stream
-//    through LDS.  Per tile a wave computes S and dP (C[q][key] layout, so
-//    lane = key and registers run over queries), then dV^T += dO^T P and
-//    dK^T += Q^T dS with P and dS taken straight from those registers as the
-//    B operand (each as a hi + lo pair of bf16 values, see below).  Q and
-//    dO are staged in LDS twice: row-major (A operand of S and dP) and
-//    transposed (A operand of dV^T and dK^T).
+//    through LDS.  Per 32-query half tile a wave computes S and dP (C[q][key]
+//    layout, so lane = key and registers run over queries), then
+//    dV^T += dO^T P and dK^T += Q^T dS with P and dS taken straight from
+//    those registers as the B operand, each as a hi + lo pair of bf16 values
+//    (see below).  Q and dO are staged in LDS twice: row-major (A operand of
+//    S and dP) and transposed (A operand of dV^T and dK^T).
 //  * bwd_q: a workgroup owns a block of queries (32 per wave) with Q, dO,
 //    LSE and D in registers and streams key tiles of 64 rows: S^T = K Q^T and
 //    dP^T = V dO^T (lane = query), dS^T, then dQ^T += K^T dS^T.  K is staged
 //    row-major and transposed, V row-major.
 // Row-major LDS tiles use an XOR swizzle of the 16-byte chunk index so that
 // both the staging writes and the operand reads are free of bank conflicts;
-// transposed tiles are padded by 16 bytes per row.
+// transposed tiles are padded by 16 bytes per row.  Tiles are read with
+// buffer loads, which return zero past the end of the head (ragged tails).
+// Working on one 32-row half tile at a time keeps the live registers of the
+// key-stationary kernel within the register file.
 #include "attn_device.h"
 #include "attn_launch.h"
 
@@ -56,12 +59,12 @@ struct Stage64 {
 
   u32x4 r[KPT];
 
-  __device__ __forceinline__ void load(const uint16_t* base, int row0, int n, int tid) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int row0, int tid) {
     const int a = tid % GROUPS, b = tid / GROUPS;
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int row = row0 + KPT * a + i;
-      r[i] = load16_or_zero(base + (size_t)row * D + 8 * b, row < n);
+      r[i] = bload16(rs, (uint32_t)row * (D * 2) + 16 * b);
     }
   }
   __device__ __forceinline__ void store_rowmajor(uint16_t* lds, int tid) const {
@@ -134,16 +137,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const uint16_t* __restri
   const int key = kw0 + l32;
 
   const size_t head = (size_t)bh * (size_t)n * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* dOh = dO + head;
-  const float* LSEh = LSE + (size_t)bh * n;
-  const float* Dh = Dsum + (size_t)bh * n;
+  const uint32_t head_bytes = (uint32_t)n * D * 2u;
+  const auto rq = make_rsrc(Q + head, head_bytes);
+  const auto rdo = make_rsrc(dO + head, head_bytes);
+  const auto rk = make_rsrc(K + head, head_bytes);
+  const auto rv = make_rsrc(V + head, head_bytes);
+  const auto rl = make_rsrc(LSE + (size_t)bh * n, (uint32_t)n * 4u);
+  const auto rd = make_rsrc(Dsum + (size_t)bh * n, (uint32_t)n * 4u);
 
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    kf[s] = as_bf16x8(load16_or_zero(K + head + (size_t)key * D + 16 * s + 8 * hh, key < n));
-    vf[s] = as_bf16x8(load16_or_zero(V + head + (size_t)key * D + 16 * s + 8 * hh, key < n));
+    kf[s] = as_bf16x8(bload16(rk, (uint32_t)key * (D * 2) + 32 * s + 16 * hh));
+    vf[s] = as_bf16x8(bload16(rv, (uint32_t)key * (D * 2) + 32 * s + 16 * hh));
   }
 
   f32x16 dva[D / 32], dka[D / 32];
@@ -158,15 +164,16 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const uint16_t* __restri
   const int ntq = (n + BQ - 1) / BQ;
   const int it0 = CAUSAL ? (k0 / BQ) : 0;
 
+  // Query rows past n load as zero (Q, dO, LSE, D), so they contribute
+  // nothing: P = 1 is finite and multiplies dO = 0 and dS = 0.
   ST sq, sd;
   float lr = 0.f, dr = 0.f;
   auto gload = [&](int i0) {
-    sq.load(Qh, i0, n, tid);
-    sd.load(dOh, i0, n, tid);
+    sq.load(rq, i0, tid);
+    sd.load(rdo, i0, tid);
     if (tid < BQ) {
-      const int row = i0 + tid;
-      lr = row < n ? LSEh[row] * kLog2e : 0.f;
-      dr = row < n ? Dh[row] : 0.f;
+      lr = bload4f(rl, (uint32_t)(i0 + tid) * 4u) * kLog2e;
+      dr = bload4f(rd, (uint32_t)(i0 + tid) * 4u);
     }
   };
   auto lstore = [&](int buf) {
@@ -180,10 +187,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const uint16_t* __restri
     }
   };
 
-  if (it0 < ntq) {
-    gload(it0 * BQ);
-    lstore(0);
-  }
+  gload(it0 * BQ);
+  lstore(0);
   __syncthreads();
 
   for (int it = it0; it < ntq; ++it) {
@@ -194,31 +199,23 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const uint16_t* __restri
     // Skip a tile whose queries all precede this wave's keys (causal).
     const bool active = !CAUSAL || (i0 + BQ - 1 >= kw0);
     if (active) {
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[t][r] = 0.f;
-          pacc[t][r] = 0.f;
-        }
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 aq = frag_rowmajor<D, KPT>(qs[buf], 32 * t + l32, s, hh);
-          const bf16x8 ad = frag_rowmajor<D, KPT>(dos[buf], 32 * t + l32, s, hh);
-          sacc[t] = mfma32(aq, kf[s], sacc[t]);
-          pacc[t] = mfma32(ad, vf[s], pacc[t]);
-        }
-
       const bool need_mask = CAUSAL && (i0 < kw0 + 31);
-      // P and dS enter dV and dK as hi + lo bf16 pairs: a single bf16
-      // rounding (relative 2^-9) of a probability near 1 can move a column
-      // sum of magnitude > 4 by more than the output's own rounding leaves.
-      bf16x8 pf[2][2], pl[2][2], df[2][2], dl[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[r] = 0.f;
+          pacc[r] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          const bf16x8 aq = frag_rowmajor<D, KPT>(qs[buf], 32 * t + l32, s, hh);
+          const bf16x8 ad = frag_rowmajor<D, KPT>(dos[buf], 32 * t + l32, s, hh);
+          sacc = mfma32(aq, kf[s], sacc);
+          pacc = mfma32(ad, vf[s], pacc);
+        }
+
         float p[16], ds[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -227,35 +224,36 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(const uint16_t* __restri
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * g + i;
-            float pv = fast_exp2(sacc[t][r] * sl2e - l4[i]);
+            float pv = fast_exp2(fmaf(sacc[r], sl2e, -l4[i]));
             if (need_mask) {
               const int q = i0 + 32 * t + 8 * g + 4 * hh + i;
               pv = key > q ? 0.f : pv;
             }
             p[r] = pv;
-            ds[r] = pv * (pacc[t][r] - d4[i]);
+            ds[r] = pv * (pacc[r] - d4[i]);
           }
         }
-        split_bf16x8(p, pf[t][0], pl[t][0]);
-        split_bf16x8(p + 8, pf[t][1], pl[t][1]);
-        split_bf16x8(ds, df[t][0], dl[t][0]);
-        split_bf16x8(ds + 8, df[t][1], dl[t][1]);
-      }
 
+        // P and dS enter dV and dK as hi + lo bf16 pairs: a single bf16
+        // rounding (relative 2^-9) of a probability near 1 can move a column
+        // sum of magnitude > 4 by more than the output's own rounding leaves.
 #pragma unroll
-      for (int e = 0; e < D / 32; ++e)
+        for (int u = 0; u < 2; ++u) {
+          bf16x8 ph, pl, dh, dl;
+          split_bf16x8(p + 8 * u, ph, pl);
+          split_bf16x8(ds + 8 * u, dh, dl);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          for (int e = 0; e < D / 32; ++e) {
             const int off = (32 * e + l32) * TSTR + 32 * t + 16 * u + 8 * hh;
             const bf16x8 adt = *reinterpret_cast<const bf16x8*>(&dots[buf][off]);
             const bf16x8 aqt = *reinterpret_cast<const bf16x8*>(&qts[buf][off]);
-            dva[e] = mfma32(adt, pf[t][u], dva[e]);
-            dka[e] = mfma32(aqt, df[t][u], dka[e]);
-            dva[e] = mfma32(adt, pl[t][u], dva[e]);
-            dka[e] = mfma32(aqt, dl[t][u], dka[e]);
+            dva[e] = mfma32(adt, ph, dva[e]);
+            dka[e] = mfma32(aqt, dh, dka[e]);
+            dva[e] = mfma32(adt, pl, dva[e]);
+            dka[e] = mfma32(aqt, dl, dka[e]);
           }
+        }
+      }
     }
 
     if (it + 1 < ntq) lstore(buf ^ 1);
@@ -312,14 +310,17 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   const int qrow = wq0 + l32;
 
   const size_t head = (size_t)bh * (size_t)n * D;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  const uint32_t head_bytes = (uint32_t)n * D * 2u;
+  const auto rq = make_rsrc(Q + head, head_bytes);
+  const auto rdo = make_rsrc(dO + head, head_bytes);
+  const auto rk = make_rsrc(K + head, head_bytes);
+  const auto rv = make_rsrc(V + head, head_bytes);
 
   bf16x8 qf[D / 16], gf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    qf[s] = as_bf16x8(load16_or_zero(Q + head + (size_t)qrow * D + 16 * s + 8 * hh, qrow < n));
-    gf[s] = as_bf16x8(load16_or_zero(dO + head + (size_t)qrow * D + 16 * s + 8 * hh, qrow < n));
+    qf[s] = as_bf16x8(bload16(rq, (uint32_t)qrow * (D * 2) + 32 * s + 16 * hh));
+    gf[s] = as_bf16x8(bload16(rdo, (uint32_t)qrow * (D * 2) + 32 * s + 16 * hh));
   }
   const float l2 = qrow < n ? LSE[(size_t)bh * n + qrow] * kLog2e : 0.f;
   const float dq_d = qrow < n ? Dsum[(size_t)bh * n + qrow] : 0.f;
@@ -335,8 +336,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 
   ST sk, sv;
   auto gload = [&](int j0) {
-    sk.load(Kh, j0, n, tid);
-    sv.load(Vh, j0, n, tid);
+    sk.load(rk, j0, tid);
+    sv.load(rv, j0, tid);
   };
   auto lstore = [&](int buf) {
     sk.store_rowmajor(ks[buf], tid);
@@ -355,52 +356,44 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 
     const bool active = !CAUSAL || (j0 <= wq0 + 31);
     if (active) {
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          sacc[t][r] = 0.f;
-          pacc[t][r] = 0.f;
-        }
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 ak = frag_rowmajor<D, KPT>(ks[buf], 32 * t + l32, s, hh);
-          const bf16x8 av = frag_rowmajor<D, KPT>(vs[buf], 32 * t + l32, s, hh);
-          sacc[t] = mfma32(ak, qf[s], sacc[t]);
-          pacc[t] = mfma32(av, gf[s], pacc[t]);
-        }
-
       const bool need_mask = (j0 + BC > n) || (CAUSAL && j0 + BC - 1 > wq0);
-      bf16x8 df[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        f32x16 sacc, pacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sacc[r] = 0.f;
+          pacc[r] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          const bf16x8 ak = frag_rowmajor<D, KPT>(ks[buf], 32 * t + l32, s, hh);
+          const bf16x8 av = frag_rowmajor<D, KPT>(vs[buf], 32 * t + l32, s, hh);
+          sacc = mfma32(ak, qf[s], sacc);
+          pacc = mfma32(av, gf[s], pacc);
+        }
+
         float ds[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float pv = fast_exp2(sacc[t][r] * sl2e - l2);
+          float pv = fast_exp2(fmaf(sacc[r], sl2e, -l2));
           if (need_mask) {
             const int kj = j0 + 32 * t + crow(r, hh);
             pv = (kj >= n || (CAUSAL && kj > qrow)) ? 0.f : pv;
           }
-          ds[r] = pv * (pacc[t][r] - dq_d);
+          ds[r] = pv * (pacc[r] - dq_d);
         }
-        df[t][0] = pack_bf16x8(ds);
-        df[t][1] = pack_bf16x8(ds + 8);
-      }
-
 #pragma unroll
-      for (int e = 0; e < D / 32; ++e)
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 df = pack_bf16x8(ds + 8 * u);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
+          for (int e = 0; e < D / 32; ++e) {
             const bf16x8 akt =
                 *reinterpret_cast<const bf16x8*>(&kts[buf][(32 * e + l32) * TSTR + 32 * t + 16 * u + 8 * hh]);
-            dqa[e] = mfma32(akt, df[t][u], dqa[e]);
+            dqa[e] = mfma32(akt, df, dqa[e]);
           }
+        }
+      }
     }
 
     if (jt + 1 < ntiles) lstore(buf ^ 1);

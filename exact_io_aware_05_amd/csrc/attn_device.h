@@ -100,6 +100,19 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
 
+// Buffer resource over `bytes` bytes at `base`: raw buffer loads through it
+// return zero for any offset at or past `bytes`, so ragged tiles need no
+// branches.  Word 3 is the gfx9 raw-buffer format (no swizzle, 32-bit data).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ float bload4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+
 // 16-byte global load with a predicate (zero when off).
 __device__ __forceinline__ u32x4 load16_or_zero(const uint16_t* p, bool ok) {
   u32x4 z = {0u, 0u, 0u, 0u};

@@ -28,8 +28,8 @@
  *     statistics are float32 [B, H, N].  Queries and keys have the same N.
  *   - Supported: d in {64, 128}; N >= 1; B, H >= 1; dtype ATTN_BF16 (bf16
  *     inputs and outputs, fp32 accumulation, outputs rounded to nearest-even)
- *     or ATTN_FP32 (fp32 throughout).  N * d must stay below 2^31 and
- *     B * H * N below 2^31.
+ *     or ATTN_FP32 (fp32 throughout).  N * d must not exceed 2^30 and
+ *     B * H * N must stay below 2^31.
  *   - The caller allocates and owns every buffer.  The library allocates no
  *     device memory; scratch memory the backward pass needs is passed in as
  *     `workspace`.

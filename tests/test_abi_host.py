@@ -75,6 +75,7 @@ def test_forward_argument_validation():
     assert _fwd(L, N=2**31) == -2
     assert _fwd(L, B=2**16, H=2**16, N=2) == -2
     assert _fwd(L, N=2**24, d=128) == -2
+    assert _fwd(L, N=2**23 + 1, d=128) == -2
     assert _fwd(L, scale=float("nan")) == -4
     assert _fwd(L, scale=float("inf")) == -4
 
