@@ -58,6 +58,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
+  const TileReader<D> TR(lane);
 
   // Logical tile: contiguous per XCD; heavy (late) query blocks first.
   const int lid = xcd_remap(blockIdx.x, total);
@@ -106,8 +107,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
       for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
-      sacc[0] = mfma32(frag_rows<D>(kb, l32, s, hh), qf[s], sacc[0]);
-      sacc[1] = mfma32(frag_rows<D>(kb, 32 + l32, s, hh), qf[s], sacc[1]);
+      sacc[0] = mfma32(TR.rows(kb, 0, s), qf[s], sacc[0]);
+      sacc[1] = mfma32(TR.rows(kb, 32, s), qf[s], sacc[1]);
     }
 
     // Mask (diagonal and ragged tiles only) and take this query's tile max.
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int e = 0; e < D / 32; ++e)
-          oacc[e] = mfma32(frag_cols<D>(vb, 32 * t + 16 * u, e, lane), pf[t][u], oacc[e]);
+          oacc[e] = mfma32(TR.cols(vb, 32 * t + 16 * u, e), pf[t][u], oacc[e]);
   };
 
   dma_tile<D, NW>(rk, k0s, 0, w, lane);

@@ -5,12 +5,10 @@
 // one-to-one on any 8 consecutive rows starting at a multiple of 8 and, on
 // any 4 consecutive rows starting at a multiple of 4, maps the chunk pairs
 // {2k, 2k+1} to 4 distinct pairs.  So both ways the kernels read a tile are
-// free of LDS bank conflicts:
-//  * frag_rows: 16 bytes = 8 consecutive features of one row per lane, rows
-//    l % 32 -- the MFMA operand whose contraction index is the feature;
-//  * frag_cols: two ds_read_b64_tr_b16 per lane, which return one feature of
-//    8 rows (in the slot order of the 32x32 result layout) -- the operand
-//    whose contraction index is the row, i.e. the transposed tile.
+// free of LDS bank conflicts: 16 bytes = 8 consecutive features of one row
+// per lane (rows l % 32), and ds_read_b64_tr_b16 pieces of 4 features x 4
+// consecutive rows per 16-lane group.
+// TileReader below gives the two read patterns.
 // Tiles are filled by 16-byte buffer->LDS DMA: lane i of a wave's load lands
 // at LDS byte 16*i after the wave's base, so each lane fetches the global
 // chunk that belongs at that position.  Rows past the end of the head read
@@ -54,35 +52,58 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* ld
   }
 }
 
-// Operand fragment of row `row` (features 16*s + 8*h .. +7).
+// Per-lane LDS byte offsets for reading MFMA operand fragments from tiles in
+// this layout.  Every fragment a kernel reads starts at a row that is a
+// multiple of 8, so the swizzle term depends only on the lane; the offsets
+// split into a few per-lane bases plus compile-time immediates:
+//  * rows(lds, rbase, s): lane l gets 8 consecutive features 16*s + 8*(l/32)
+//    .. +7 of row rbase + l % 32 (operand whose contraction index is the
+//    feature).  Chunk 2s + h XOR w equals 8*(s/4) + ((2*(s%4) + h) XOR w).
+//  * cols(lds, rbase, e): lane l (half h = l / 32) gets feature
+//    32*e + l % 32 of the 8 rows rbase + {4h .. 4h+3, 8+4h .. 8+4h+3}, in that
+//    order -- rows in the slot order of the 32x32 result layout, so the
+//    fragment pairs with result registers 8u..8u+7 when rbase = 32t + 16u
+//    (operand whose contraction index is the row, i.e. the transposed tile).
+//    Two ds_read_b64_tr_b16: within each 16-lane group the hardware hands lane
+//    i element i % 4 of the 8-byte piece addressed by lane 4s + i/4, so lane
+//    j = 4s + c addresses row (4h + s) and features 4c .. 4c+3 of its group's
+//    16-feature slice.
 template <int D>
-__device__ __forceinline__ bf16x8 frag_rows(const uint16_t* lds, int row, int s, int h) {
-  return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(lds) + tile_off<D>(row, 2 * s + h));
-}
+struct TileReader {
+  uint32_t row_base[4];
+  uint32_t col_base[2];
 
-// Transposed operand fragment: lane l (half h = l / 32) receives feature
-// f = 32 * e + l % 32 of the 8 rows rbase + {4h .. 4h+3, 8+4h .. 8+4h+3},
-// in that order -- rows in the slot order of the 32x32 result layout, so
-// the fragment pairs with result registers 8u..8u+7 when rbase = 32t + 16u.
-// Within each 16-lane group the hardware hands lane i element i % 4 of the
-// 8-byte piece addressed by lane 4s + i/4, for s = 0..3.
-template <int D>
-__device__ __forceinline__ bf16x8 frag_cols(const uint16_t* lds, int rbase, int e, int lane) {
-  const int g = lane >> 4, i16 = lane & 15;
-  const int h = g >> 1;
-  const int col = 32 * e + 16 * (g & 1) + 4 * (i16 & 3);  // first of 4 features this lane addresses
-  const int r0 = rbase + 4 * h + (i16 >> 2);
-  const char* base = reinterpret_cast<const char*>(lds);
-  const uint32_t o0 = tile_off<D>(r0, col >> 3) + 2 * (col & 7);
-  const uint32_t o1 = tile_off<D>(r0 + 8, col >> 3) + 2 * (col & 7);
-  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)(base + o0));
-  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)(base + o1));
-  u32x4 u;
-  u[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1));
-  u[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3));
-  u[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 0, 1));
-  u[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 2, 3));
-  return as_bf16x8(u);
-}
+  __device__ __forceinline__ explicit TileReader(int lane) {
+    const int l32 = lane & 31, h = lane >> 5;
+    const int w = tile_swz(l32);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      row_base[k] = (uint32_t)(l32 * (D * 2) + 16 * ((2 * k + h) ^ w));
+    const int g = lane >> 4, i16 = lane & 15;
+    const int r0 = 4 * h + (i16 >> 2);
+    const int z = 2 * (g & 1) + ((i16 & 3) >> 1);
+    const int wc = tile_swz(r0);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      col_base[p] = (uint32_t)(r0 * (D * 2) + 16 * ((4 * p + z) ^ wc) + 8 * (i16 & 1));
+  }
+
+  __device__ __forceinline__ bf16x8 rows(const uint16_t* lds, int rbase, int s) const {
+    const char* p = reinterpret_cast<const char*>(lds) + row_base[s & 3] + rbase * (D * 2) + 128 * (s >> 2);
+    return *reinterpret_cast<const bf16x8*>(p);
+  }
+
+  __device__ __forceinline__ bf16x8 cols(const uint16_t* lds, int rbase, int e) const {
+    const char* p = reinterpret_cast<const char*>(lds) + col_base[e & 1] + rbase * (D * 2) + 128 * (e >> 1);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)p);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)(p + 8 * D * 2));
+    u32x4 u;
+    u[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1));
+    u[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3));
+    u[2] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 0, 1));
+    u[3] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(b, b, 2, 3));
+    return as_bf16x8(u);
+  }
+};
 
 }  // namespace attn
