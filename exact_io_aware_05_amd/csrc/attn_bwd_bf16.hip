@@ -47,6 +47,10 @@ namespace {
 // accumulators), so two waves fit per SIMD and one's matrix work overlaps
 // the other's vector work.
 // ---------------------------------------------------------------------------
+// Magnitude from which P and dS enter the dV and dK products as hi + lo bf16
+// pairs (see bwd_kv_kernel).
+constexpr float kSplitThreshold = 1.0f / 16.0f;
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ K,
@@ -68,7 +72,8 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) float lse0s[BQ], dsm0s[BQ], lse1s[BQ], dsm1s[BQ];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int hh = lane >> 5, l32 = lane & 31;
   const TileReader<D> TR(lane);
   const int grp = w & 3;        // key group: keys 32*grp .. +31 of the block
@@ -138,9 +143,20 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     if (active) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
+        // The dP wave accumulates onto -D (registers run over queries), so
+        // it ends with dP - D directly.
         f32x16 c;
+        if (s_role) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) c[r] = 0.f;
+          for (int r = 0; r < 16; ++r) c[r] = 0.f;
+        } else {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsms[32 * t + 8 * g + 4 * hh]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c[4 * g + i] = -d4[i];
+          }
+        }
         const uint16_t* as = s_role ? qs : gs;
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) c = mfma32(TR.rows(as, 32 * t, s), bf[s], c);
@@ -175,26 +191,40 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
           // dS = P * (dP - D)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsms[32 * t + 8 * g + 4 * hh]);
             const f32x4 p4 = *reinterpret_cast<const f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[t][4 * g + i] = p4[i] * (v[t][4 * g + i] - d4[i]);
+            for (int i = 0; i < 4; ++i) v[t][4 * g + i] = p4[i] * v[t][4 * g + i];
           }
         }
-        // P (or dS) enters dV (or dK) as a hi + lo pair of bf16 values: a
-        // single bf16 rounding (relative 2^-9) of a probability near 1 can
-        // move a column sum of magnitude > 4 by more than the output's own
-        // rounding leaves.
+        // P (or dS) enters dV (or dK) as a hi + lo pair of bf16 values
+        // wherever this half tile holds a magnitude >= 1/16: a single bf16
+        // rounding (relative 2^-9) of a probability near 1 can move a column
+        // sum of magnitude > 4 by more than the output's own rounding leaves,
+        // while tiles of small values (long rows, away from the causal
+        // diagonal) lose nothing measurable with one bf16 term.  The test is
+        // wave-uniform (ballot).
         const uint16_t* bs = s_role ? gs : qs;  // dO^T for dV, Q^T for dK
+        float vmax = 0.f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          bf16x8 hi, lo;
-          split_bf16x8(&v[t][8 * u], hi, lo);
+        for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, fabsf(v[t][r]));
+        if (__builtin_amdgcn_ballot_w64(vmax >= kSplitThreshold) != 0) {
 #pragma unroll
-          for (int e = 0; e < D / 32; ++e) {
-            const bf16x8 a = TR.cols(bs, 32 * t + 16 * u, e);
-            acc[e] = mfma32(a, hi, acc[e]);
-            acc[e] = mfma32(a, lo, acc[e]);
+          for (int u = 0; u < 2; ++u) {
+            bf16x8 hi, lo;
+            split_bf16x8(&v[t][8 * u], hi, lo);
+#pragma unroll
+            for (int e = 0; e < D / 32; ++e) {
+              const bf16x8 a = TR.cols(bs, 32 * t + 16 * u, e);
+              acc[e] = mfma32(a, hi, acc[e]);
+              acc[e] = mfma32(a, lo, acc[e]);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const bf16x8 hi = pack_bf16x8(&v[t][8 * u]);
+#pragma unroll
+            for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(TR.cols(bs, 32 * t + 16 * u, e), hi, acc[e]);
           }
         }
       }
@@ -249,7 +279,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   __shared__ __attribute__((aligned(1024))) uint16_t v1s[BC * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const TileReader<D> TR(lane);
 
@@ -291,6 +322,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
     const bool need_mask = (j0 + BC > n) || (CAUSAL && j0 + BC - 1 > wq0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      // One half tile at a time: interleaving the halves costs more
+      // registers than the file holds at two waves per SIMD.
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -371,9 +405,13 @@ hipError_t launch_dkdv(const BwdArgs& a) {
   return hipGetLastError();
 }
 
+#ifndef ATTN_DQ_NW128
+#define ATTN_DQ_NW128 8  // waves per dQ workgroup at d = 128 (tuning knob)
+#endif
+
 template <int D, bool CAUSAL>
 hipError_t launch_dq(const BwdArgs& a) {
-  constexpr int NW = D == 128 ? 8 : 4;
+  constexpr int NW = D == 128 ? ATTN_DQ_NW128 : 4;
   const int n = (int)a.n;
   const int nqb = (n + NW * 32 - 1) / (NW * 32);
   const int total = (int)(a.bh * nqb);

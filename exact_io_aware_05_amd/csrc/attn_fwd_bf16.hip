@@ -56,7 +56,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   __shared__ __attribute__((aligned(1024))) uint16_t v1s[BC * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int l32 = lane & 31, hh = lane >> 5;
   const TileReader<D> TR(lane);
 

@@ -1,13 +1,18 @@
 // LDS tiles of 64 rows x D bf16 features, shared by the gfx950 kernels.
 //
-// Layout: row-major, no padding, with the 16-byte chunk index of each row
-// XORed with swz(row) = 2*(row & 3) + ((row >> 2) & 1).  That permutation is
-// one-to-one on any 8 consecutive rows starting at a multiple of 8 and, on
-// any 4 consecutive rows starting at a multiple of 4, maps the chunk pairs
-// {2k, 2k+1} to 4 distinct pairs.  So both ways the kernels read a tile are
-// free of LDS bank conflicts: 16 bytes = 8 consecutive features of one row
-// per lane (rows l % 32), and ds_read_b64_tr_b16 pieces of 4 features x 4
-// consecutive rows per 16-lane group.
+// Layout: row-major, no padding, with the 16-byte chunk index c of each row
+// replaced by c XOR tile_swz<D>(row).  The gfx950 LDS serves 256 bytes per
+// clock (64 banks of 4 bytes); a 16-byte read is resolved 16 lanes at a time
+// and an 8-byte transposing read 32 lanes at a time.  The swizzle makes both
+// ways the kernels read a tile conflict-free:
+//  * row reads: 16 consecutive lanes read the same chunk of 16 consecutive
+//    rows -- the swizzle is one-to-one on any 16 consecutive rows (counting
+//    the two half-lines of a 256-byte line separately when D = 64);
+//  * transposed reads: 32 lanes read chunks 4e .. 4e+3 of 4 consecutive rows
+//    (starting at a multiple of 4) -- the swizzle sends the 4 rows' groups of
+//    4 chunks to disjoint bank ranges.
+// D = 128 (256-byte rows): tile_swz = 4 * (row % 4) + (row / 4) % 4.
+// D = 64 (128-byte rows): tile_swz = 4 * ((row / 2) % 2) + (row / 4) % 4.
 // TileReader below gives the two read patterns.
 // Tiles are filled by 16-byte buffer->LDS DMA: lane i of a wave's load lands
 // at LDS byte 16*i after the wave's base, so each lane fetches the global
@@ -22,12 +27,16 @@ namespace attn {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define ATTN_LDS __attribute__((address_space(3)))
 
-__device__ __forceinline__ constexpr int tile_swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+template <int D>
+__device__ __forceinline__ constexpr int tile_swz(int row) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : (((row & 2) << 1) | ((row >> 2) & 3));
+}
 
 // Byte offset of (row, 16-byte chunk c) in a tile with D features per row.
 template <int D>
 __device__ __forceinline__ constexpr uint32_t tile_off(int row, int c) {
-  return (uint32_t)(row * (D * 2) + 16 * (c ^ tile_swz(row)));
+  return (uint32_t)(row * (D * 2) + 16 * (c ^ tile_swz<D>(row)));
 }
 
 // Wait for this wave's outstanding vector-memory operations (LDS DMA
@@ -46,7 +55,7 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* ld
     const int k = w * IPW + r;
     const int p = 64 * k + lane;          // LDS chunk this lane fills
     const int row = p / CPR, cp = p % CPR;
-    const int c = cp ^ tile_swz(row);     // global chunk that belongs there
+    const int c = cp ^ tile_swz<D>(row);  // global chunk that belongs there
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(lds + 512 * k), 16,
                                              (uint32_t)(row0 + row) * (D * 2) + 16 * c, 0, 0, 0);
   }
@@ -54,11 +63,11 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* ld
 
 // Per-lane LDS byte offsets for reading MFMA operand fragments from tiles in
 // this layout.  Every fragment a kernel reads starts at a row that is a
-// multiple of 8, so the swizzle term depends only on the lane; the offsets
-// split into a few per-lane bases plus compile-time immediates:
+// multiple of 16, so the swizzle term depends only on the lane and the
+// offsets are a few per-lane bases plus compile-time immediates:
 //  * rows(lds, rbase, s): lane l gets 8 consecutive features 16*s + 8*(l/32)
 //    .. +7 of row rbase + l % 32 (operand whose contraction index is the
-//    feature).  Chunk 2s + h XOR w equals 8*(s/4) + ((2*(s%4) + h) XOR w).
+//    feature).
 //  * cols(lds, rbase, e): lane l (half h = l / 32) gets feature
 //    32*e + l % 32 of the 8 rows rbase + {4h .. 4h+3, 8+4h .. 8+4h+3}, in that
 //    order -- rows in the slot order of the 32x32 result layout, so the
@@ -70,33 +79,37 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* ld
 //    16-feature slice.
 template <int D>
 struct TileReader {
-  uint32_t row_base[4];
-  uint32_t col_base[2];
+  static constexpr int NS = D / 16;  // row fragments per row
+  static constexpr int NE = D / 32;  // transposed fragments per 32 features
+  uint32_t row_base[NS];
+  uint32_t col_base[NE][2];
 
   __device__ __forceinline__ explicit TileReader(int lane) {
     const int l32 = lane & 31, h = lane >> 5;
-    const int w = tile_swz(l32);
+    const int w = tile_swz<D>(l32);
 #pragma unroll
-    for (int k = 0; k < 4; ++k)
-      row_base[k] = (uint32_t)(l32 * (D * 2) + 16 * ((2 * k + h) ^ w));
+    for (int s = 0; s < NS; ++s) row_base[s] = (uint32_t)(l32 * (D * 2) + 16 * ((2 * s + h) ^ w));
     const int g = lane >> 4, i16 = lane & 15;
     const int r0 = 4 * h + (i16 >> 2);
     const int z = 2 * (g & 1) + ((i16 & 3) >> 1);
-    const int wc = tile_swz(r0);
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
-      col_base[p] = (uint32_t)(r0 * (D * 2) + 16 * ((4 * p + z) ^ wc) + 8 * (i16 & 1));
+    for (int e = 0; e < NE; ++e)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int r = r0 + 8 * k;
+        col_base[e][k] = (uint32_t)(r * (D * 2) + 16 * ((4 * e + z) ^ tile_swz<D>(r)) + 8 * (i16 & 1));
+      }
   }
 
   __device__ __forceinline__ bf16x8 rows(const uint16_t* lds, int rbase, int s) const {
-    const char* p = reinterpret_cast<const char*>(lds) + row_base[s & 3] + rbase * (D * 2) + 128 * (s >> 2);
+    const char* p = reinterpret_cast<const char*>(lds) + row_base[s] + rbase * (D * 2);
     return *reinterpret_cast<const bf16x8*>(p);
   }
 
   __device__ __forceinline__ bf16x8 cols(const uint16_t* lds, int rbase, int e) const {
-    const char* p = reinterpret_cast<const char*>(lds) + col_base[e & 1] + rbase * (D * 2) + 128 * (e >> 1);
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)p);
-    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)(p + 8 * D * 2));
+    const char* p = reinterpret_cast<const char*>(lds) + rbase * (D * 2);
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)(p + col_base[e][0]));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)(p + col_base[e][1]));
     u32x4 u;
     u[0] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 0, 1));
     u[1] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(a, a, 2, 3));

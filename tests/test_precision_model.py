@@ -45,3 +45,33 @@ def test_single_bf16_probabilities_exceed_tolerance_and_hilo_does_not():
     assert err_bf16 > 2e-2
     assert err_hilo < 1.2 * err_floor + 1e-3
     assert err_hilo < 1.5e-2
+
+
+def _selective(p, tau=1.0 / 16, tq=32, tk=32):
+    """hi + lo only on 32 x 32 tiles holding a value >= tau, as the kernel does."""
+    out = _bf16(p)
+    full = _hilo(p)
+    for i in range(0, p.shape[0], tq):
+        for j in range(0, p.shape[1], tk):
+            if np.abs(p[i : i + tq, j : j + tk]).max() >= tau:
+                out[i : i + tq, j : j + tk] = full[i : i + tq, j : j + tk]
+    return out
+
+
+def test_selective_split_keeps_the_full_split_accuracy():
+    """Splitting only tiles with a probability >= 1/16 loses nothing measurable."""
+    shape, causal = (2, 2, 129, 128), True
+    seed = 2000 + sum(shape) + 11
+    inp = synth.qkvdo(seed, shape, "bf16")
+    scale = 1.0 / math.sqrt(shape[3])
+    q, k, do = inp["q"], inp["k"], inp["do"]
+    _, lse = A.forward(q, k, inp["v"], causal, scale)
+    _, _, dv_ref = A.backward(q, k, inp["v"], do, causal, scale)
+    err_sel, err_hilo = 0.0, 0.0
+    for b in range(shape[0]):
+        for h in range(shape[1]):
+            p = np.exp(A.scores(q[b, h], k[b, h], scale, causal) - lse[b, h][:, None])
+            ref = dv_ref[b, h]
+            err_sel = max(err_sel, np.abs(_bf16(_selective(p).T @ do[b, h]) - ref).max())
+            err_hilo = max(err_hilo, np.abs(_bf16(_hilo(p).T @ do[b, h]) - ref).max())
+    assert err_sel <= err_hilo + 1e-4
