@@ -113,7 +113,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   // Query rows past n load as zero (Q, dO, LSE, D), so they contribute
   // nothing: P = 1 is finite and multiplies dO = 0 and dS = 0.
   float lr = 0.f, dr = 0.f;
-  auto issue = [&](uint16_t* qd, uint16_t* gd, int i0) {
+  auto issue = [&](uint16_t* qd, uint16_t* gd, int i0) ATTN_INLINE {
     dma_tile<D, NW>(rq, qd, i0, w, lane);
     dma_tile<D, NW>(rdo, gd, i0, w, lane);
     if (tid < BQ) {
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
       dr = bload4f(rd, (uint32_t)(i0 + tid) * 4u);
     }
   };
-  auto publish = [&](float* ld, float* dd) {
+  auto publish = [&](float* ld, float* dd) ATTN_INLINE {
     if (tid < BQ) {
       ld[tid] = lr;
       dd[tid] = dr;
@@ -132,116 +132,152 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 
   float* px = pxs + grp * (2 * 4 * 64 * 4);
 
-  auto compute = [&](const uint16_t* qs, const uint16_t* gs, const float* lse2s, const float* dsms, int i0) {
-    // A tile whose queries all precede this key group is skipped (causal).
-    // The test is uniform over the workgroup's barrier participants: both
-    // waves of a pair take the same branch, and the mid-tile barrier below is
-    // reached by every wave.
-    const bool active = !CAUSAL || (i0 + BQ - 1 >= kw0);
-    const bool need_mask = CAUSAL && (i0 < kw0 + 31);
-    float v[2][16];  // P (S wave) or dP (dP wave), per half tile
-    if (active) {
+  // P or dS of one half tile into dV or dK: hi + lo bf16 pairs where the
+  // half tile holds a magnitude >= 1/16 (a single bf16 rounding, relative
+  // 2^-9, of a probability near 1 can move a column sum of magnitude > 4 by
+  // more than the output's own rounding leaves), one bf16 term elsewhere
+  // (long rows, away from the causal diagonal, lose nothing measurable).
+  // The test is wave-uniform (ballot).
+  auto accumulate = [&](const uint16_t* bs, const float* vt, int t) ATTN_INLINE {
+    __builtin_amdgcn_sched_barrier(0);
+    float vmax = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        // The dP wave accumulates onto -D (registers run over queries), so
-        // it ends with dP - D directly.
-        f32x16 c;
-        if (s_role) {
+    for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, fabsf(vt[r]));
+    if (__builtin_amdgcn_ballot_w64(vmax >= kSplitThreshold) != 0) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) c[r] = 0.f;
-        } else {
+      for (int u = 0; u < 2; ++u) {
+        bf16x8 hi, lo;
+        split_bf16x8(vt + 8 * u, hi, lo);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsms[32 * t + 8 * g + 4 * hh]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) c[4 * g + i] = -d4[i];
-          }
-        }
-        const uint16_t* as = s_role ? qs : gs;
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) c = mfma32(TR.rows(as, 32 * t, s), bf[s], c);
-        if (s_role) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * t + 8 * g + 4 * hh]);
-            f32x4 o;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float pv = fast_exp2(fmaf(c[4 * g + i], sl2e, -l4[i]));
-              if (need_mask) {
-                const int q = i0 + 32 * t + 8 * g + 4 * hh + i;
-                pv = key > q ? 0.f : pv;
-              }
-              v[t][4 * g + i] = pv;
-              o[i] = pv;
-            }
-            *reinterpret_cast<f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]) = o;
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[t][r] = c[r];
+        for (int e = 0; e < D / 32; ++e) {
+          const bf16x8 a = TR.cols(bs, 32 * t + 16 * u, e);
+          acc[e] = mfma32(a, hi, acc[e]);
+          acc[e] = mfma32(a, lo, acc[e]);
         }
       }
-    }
-    __syncthreads();  // P of this tile is visible to the dP waves
-    if (active) {
+    } else {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        if (!s_role) {
-          // dS = P * (dP - D)
+      for (int u = 0; u < 2; ++u) {
+        const bf16x8 hi = pack_bf16x8(vt + 8 * u);
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[t][4 * g + i] = p4[i] * v[t][4 * g + i];
-          }
-        }
-        // P (or dS) enters dV (or dK) as a hi + lo pair of bf16 values
-        // wherever this half tile holds a magnitude >= 1/16: a single bf16
-        // rounding (relative 2^-9) of a probability near 1 can move a column
-        // sum of magnitude > 4 by more than the output's own rounding leaves,
-        // while tiles of small values (long rows, away from the causal
-        // diagonal) lose nothing measurable with one bf16 term.  The test is
-        // wave-uniform (ballot).
-        const uint16_t* bs = s_role ? gs : qs;  // dO^T for dV, Q^T for dK
-        float vmax = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, fabsf(v[t][r]));
-        if (__builtin_amdgcn_ballot_w64(vmax >= kSplitThreshold) != 0) {
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            bf16x8 hi, lo;
-            split_bf16x8(&v[t][8 * u], hi, lo);
-#pragma unroll
-            for (int e = 0; e < D / 32; ++e) {
-              const bf16x8 a = TR.cols(bs, 32 * t + 16 * u, e);
-              acc[e] = mfma32(a, hi, acc[e]);
-              acc[e] = mfma32(a, lo, acc[e]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 hi = pack_bf16x8(&v[t][8 * u]);
-#pragma unroll
-            for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(TR.cols(bs, 32 * t + 16 * u, e), hi, acc[e]);
-          }
-        }
+        for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(TR.cols(bs, 32 * t + 16 * u, e), hi, acc[e]);
       }
     }
   };
 
-  issue(q0s, g0s, it0 * BQ);
-  publish(lse0s, dsm0s);
+  // S wave: S = Q K^T for both half tiles (two independent MFMA chains
+  // sharing each K fragment), P = exp(S - LSE) published through LDS, then
+  // dV^T += dO^T P.
+  auto compute_s = [&](const uint16_t* qs, const uint16_t* gs, const float* lse2s, int i0, bool active,
+                       bool need_mask) ATTN_INLINE {
+    float v[2][16];
+    if (active) {
+      f32x16 c0, c1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        c0[r] = 0.f;
+        c1[r] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        c0 = mfma32(TR.rows(qs, 0, s), bf[s], c0);
+        c1 = mfma32(TR.rows(qs, 32, s), bf[s], c1);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * t + 8 * g + 4 * hh]);
+          f32x4 o;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float pv = fast_exp2(fmaf(t == 0 ? c0[4 * g + i] : c1[4 * g + i], sl2e, -l4[i]));
+            if (need_mask) {
+              const int q = i0 + 32 * t + 8 * g + 4 * hh + i;
+              pv = key > q ? 0.f : pv;
+            }
+            v[t][4 * g + i] = pv;
+            o[i] = pv;
+          }
+          *reinterpret_cast<f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]) = o;
+        }
+    }
+    __syncthreads();  // P of this tile is visible to the dP waves
+    if (active) {
+      accumulate(gs, v[0], 0);
+      accumulate(gs, v[1], 1);
+    }
+  };
 
-  for (int it = it0; it < ntq; it += 2) {
-    if (it + 1 < ntq) issue(q1s, g1s, (it + 1) * BQ);
-    compute(q0s, g0s, lse0s, dsm0s, it * BQ);
-    publish(lse1s, dsm1s);
-    if (it + 1 >= ntq) break;
-    if (it + 2 < ntq) issue(q0s, g0s, (it + 2) * BQ);
-    compute(q1s, g1s, lse1s, dsm1s, (it + 1) * BQ);
+  // dP wave: dP = dO V^T accumulated onto -D (registers run over queries),
+  // so it ends with dP - D; after P arrives, dS = P * (dP - D), then
+  // dK^T += Q^T dS.
+  auto compute_dp = [&](const uint16_t* qs, const uint16_t* gs, const float* dsms, bool active) ATTN_INLINE {
+    float v[2][16];
+    if (active) {
+      f32x16 c0, c1;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dsms[8 * g + 4 * hh]);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dsms[32 + 8 * g + 4 * hh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          c0[4 * g + i] = -d0[i];
+          c1[4 * g + i] = -d1[i];
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        c0 = mfma32(TR.rows(gs, 0, s), bf[s], c0);
+        c1 = mfma32(TR.rows(gs, 32, s), bf[s], c1);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        v[0][r] = c0[r];
+        v[1][r] = c1[r];
+      }
+    }
+    __syncthreads();  // P of this tile is ready
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 p4 = *reinterpret_cast<const f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[t][4 * g + i] *= p4[i];
+        }
+        accumulate(qs, v[t], t);
+      }
+    }
+  };
+
+  // The tile loop, once per role: each role's loop is its own region for the
+  // register allocator (the two roles together would not fit), and both run
+  // the same sequence of barriers.  A tile whose queries all precede this key
+  // group is skipped (causal); both waves of a pair decide alike, and every
+  // wave reaches the mid-tile barrier inside compute_s / compute_dp.
+  auto run = [&](auto&& compute) ATTN_INLINE {
+    issue(q0s, g0s, it0 * BQ);
     publish(lse0s, dsm0s);
+    for (int it = it0; it < ntq; it += 2) {
+      if (it + 1 < ntq) issue(q1s, g1s, (it + 1) * BQ);
+      compute(q0s, g0s, lse0s, dsm0s, it * BQ);
+      publish(lse1s, dsm1s);
+      if (it + 1 >= ntq) break;
+      if (it + 2 < ntq) issue(q0s, g0s, (it + 2) * BQ);
+      compute(q1s, g1s, lse1s, dsm1s, (it + 1) * BQ);
+      publish(lse0s, dsm0s);
+    }
+  };
+  if (s_role) {
+    run([&](const uint16_t* qs, const uint16_t* gs, const float* lse2s, const float*, int i0) ATTN_INLINE {
+      compute_s(qs, gs, lse2s, i0, !CAUSAL || (i0 + BQ - 1 >= kw0), CAUSAL && (i0 < kw0 + 31));
+    });
+  } else {
+    run([&](const uint16_t* qs, const uint16_t* gs, const float*, const float* dsms, int i0) ATTN_INLINE {
+      compute_dp(qs, gs, dsms, !CAUSAL || (i0 + BQ - 1 >= kw0));
+    });
   }
 
   if (key < n) {

@@ -13,6 +13,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Lambdas that capture a kernel's register arrays by reference must be
+// inlined, or the arrays are placed in scratch memory.
+#define ATTN_INLINE __attribute__((always_inline))
+
 namespace attn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
