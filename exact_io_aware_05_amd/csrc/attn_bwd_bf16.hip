@@ -25,6 +25,8 @@
 // Tiles come from buffer->LDS DMA into two buffers (the next tile streams in
 // while the current one is used; rows past the end of the head arrive as
 // zeros).
+#include <type_traits>
+
 #include "attn_device.h"
 #include "attn_launch.h"
 #include "attn_tile.h"
@@ -46,10 +48,51 @@ namespace {
 // Each wave keeps only its half of the state (K or V fragments, dV or dK
 // accumulators), so two waves fit per SIMD and one's matrix work overlaps
 // the other's vector work.
+//
+// Per tile there are two barriers: one after P is published (mid-tile), one
+// at the hand-over to the next tile.  Between them the S wave has its
+// exponentials (before the mid-tile barrier) and the dP wave its dS products
+// (after it); to keep the matrix cores busy through both, the dP wave defers
+// the dK products of each tile to the first half of the next tile, where
+// they run beside the S wave's exponentials.  That keeps a tile's Q one tile
+// longer in LDS: Q and dO tiles are triple-buffered, and the DMA of tile
+// i + 2 is issued once the mid-tile barrier of tile i has retired the reads
+// of tile i - 1.
 // ---------------------------------------------------------------------------
 // Magnitude from which P and dS enter the dV and dK products as hi + lo bf16
 // pairs (see bwd_kv_kernel).
 constexpr float kSplitThreshold = 1.0f / 16.0f;
+
+// Schedule hint for a block of M operand reads feeding M MFMAs: issue half of
+// the reads up front, then alternate MFMA and read, so each read is in flight
+// for several MFMAs before its result is needed.
+template <int M>
+__device__ __forceinline__ void pipeline_reads() {
+  constexpr int AHEAD = M / 2;
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < M - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+// Same, for MFMAs whose operand takes two reads.
+template <int M>
+__device__ __forceinline__ void pipeline_reads2() {
+  constexpr int AHEAD = M / 2;
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < M - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
+template <int N>
+using int_c = std::integral_constant<int, N>;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restrict__ Q,
@@ -61,21 +104,32 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
                                                         uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                                                         int n, int nkb, int total, float scale, float sl2e) {
   constexpr int NW = 8, BKV = 128, BQ = 64;
+  constexpr int TB = BQ * D * 2;  // bytes per 64-row tile
+  constexpr int IPW = (D / 8) / NW;  // DMA loads per wave per tile
 
-  __shared__ __attribute__((aligned(1024))) uint16_t q0s[BQ * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t g0s[BQ * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t q1s[BQ * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t g1s[BQ * D];
-  // P of the current tile, per key group and half tile, lane-major:
-  // [group][t][r / 4][lane][r % 4].
-  __shared__ __attribute__((aligned(1024))) float pxs[4 * 2 * 4 * 64 * 4];
-  __shared__ __attribute__((aligned(16))) float lse0s[BQ], dsm0s[BQ], lse1s[BQ], dsm1s[BQ];
+  // LDS, carved by hand:
+  //   [0, 2 KiB)     LSE (x log2 e) and D of up to three query tiles,
+  //   Q tiles 0-2, then dO tiles 0-2 (64 rows x D bf16 each),
+  //   P exchange     per key group and half tile, lane-major:
+  //                  [group][t][r / 4][lane][r % 4] fp32.
+  // Reads of the dO tiles go through readers shifted by 3 tiles, so that
+  // every tile read uses an immediate offset below 64 KiB.
+  constexpr int SMALL = 2048, GSHIFT = 3 * TB;
+  __shared__ __attribute__((aligned(1024))) char smem[SMALL + 6 * TB + 4 * 2 * 4 * 64 * 4 * 4];
+  auto lse_at = [&](auto b) ATTN_INLINE { return reinterpret_cast<float*>(smem + 512 * decltype(b)::value); };
+  auto dsm_at = [&](auto b) ATTN_INLINE { return reinterpret_cast<float*>(smem + 512 * decltype(b)::value + 256); };
+  auto q_at = [&](auto b) ATTN_INLINE {
+    return reinterpret_cast<uint16_t*>(smem + SMALL + TB * decltype(b)::value);
+  };
+  auto g_at = [&](auto b) ATTN_INLINE {
+    return reinterpret_cast<uint16_t*>(smem + SMALL + TB * (3 + decltype(b)::value));
+  };
+  float* const pxs = reinterpret_cast<float*>(smem + SMALL + 6 * TB);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int hh = lane >> 5, l32 = lane & 31;
-  const TileReader<D> TR(lane);
   const int grp = w & 3;        // key group: keys 32*grp .. +31 of the block
   const bool s_role = w < 4;    // S wave (dV) or dP wave (dK)
 
@@ -109,175 +163,230 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 
   const int ntq = (n + BQ - 1) / BQ;
   const int it0 = CAUSAL ? (k0 / BQ) : 0;
+  // A tile whose queries all precede this key group is skipped (causal);
+  // both waves of a pair decide alike.
+  auto active = [&](int i) ATTN_INLINE { return !CAUSAL || (i * BQ + BQ - 1 >= kw0); };
 
   // Query rows past n load as zero (Q, dO, LSE, D), so they contribute
   // nothing: P = 1 is finite and multiplies dO = 0 and dS = 0.
   float lr = 0.f, dr = 0.f;
-  auto issue = [&](uint16_t* qd, uint16_t* gd, int i0) ATTN_INLINE {
-    dma_tile<D, NW>(rq, qd, i0, w, lane);
-    dma_tile<D, NW>(rdo, gd, i0, w, lane);
+  auto load_small = [&](int i) ATTN_INLINE {
     if (tid < BQ) {
-      lr = bload4f(rl, (uint32_t)(i0 + tid) * 4u) * kLog2e;
-      dr = bload4f(rd, (uint32_t)(i0 + tid) * 4u);
+      const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)i * (BQ * 4)) + (uint32_t)tid * 4u;
+      lr = bload4f(rl, off) * kLog2e;
+      dr = bload4f(rd, off);
     }
   };
-  auto publish = [&](float* ld, float* dd) ATTN_INLINE {
+  auto store_small = [&](auto b) ATTN_INLINE {
     if (tid < BQ) {
-      ld[tid] = lr;
-      dd[tid] = dr;
+      lse_at(b)[tid] = lr;
+      dsm_at(b)[tid] = dr;
     }
-    wait_vmem();
+  };
+  auto dma = [&](int i, auto b) ATTN_INLINE {
+    dma_tile<D, NW>(rq, q_at(b), i * BQ, w, lane);
+    dma_tile<D, NW>(rdo, g_at(b), i * BQ, w, lane);
+  };
+  // End of a tile: the DMA of the next tile must have landed; the one of
+  // the tile after it (2 * IPW loads, issued last) may still be in flight.
+  auto handover = [&](bool more) ATTN_INLINE {
+    if (more)
+      wait_vmem_upto<2 * IPW>();
+    else
+      wait_vmem();
     __syncthreads();
   };
 
   float* px = pxs + grp * (2 * 4 * 64 * 4);
 
-  // P or dS of one half tile into dV or dK: hi + lo bf16 pairs where the
-  // half tile holds a magnitude >= 1/16 (a single bf16 rounding, relative
-  // 2^-9, of a probability near 1 can move a column sum of magnitude > 4 by
-  // more than the output's own rounding leaves), one bf16 term elsewhere
-  // (long rows, away from the causal diagonal, lose nothing measurable).
-  // The test is wave-uniform (ballot).
-  auto accumulate = [&](const uint16_t* bs, const float* vt, int t) ATTN_INLINE {
+  // Products of P or dS for one half tile into dV or dK.  Where the half
+  // tile holds a magnitude >= 1/16 the values enter as hi + lo bf16 pairs (a
+  // single bf16 rounding, relative 2^-9, of a probability near 1 can move a
+  // column sum of magnitude > 4 by more than the output's own rounding
+  // leaves); each term is one call, with packed operands h[u].
+  auto acc_plain = [&](auto& tr, const uint16_t* bs, const bf16x8* h, int t) ATTN_INLINE {
     __builtin_amdgcn_sched_barrier(0);
+    bf16x8 a[2][D / 32];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) a[u][e] = tr.cols(bs, 32 * t + 16 * u, e);
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[0][e], h[0], acc[e]);
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[1][e], h[1], acc[e]);
+    pipeline_reads2<D / 16>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Wave-uniform test for the split.
+  auto needs_split = [&](const float* vt) ATTN_INLINE {
     float vmax = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, fabsf(vt[r]));
-    if (__builtin_amdgcn_ballot_w64(vmax >= kSplitThreshold) != 0) {
+    return __builtin_amdgcn_ballot_w64(vmax >= kSplitThreshold) != 0;
+  };
+  // Two independent MFMA chains (queries 0-31 and 32-63 of the tile) over
+  // the row-major tile `src`, with this wave's key-side fragments.
+  auto chains = [&](auto& tr, const uint16_t* src, f32x16& c0, f32x16& c1) ATTN_INLINE {
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 a0[D / 16], a1[D / 16];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        bf16x8 hi, lo;
-        split_bf16x8(vt + 8 * u, hi, lo);
-#pragma unroll
-        for (int e = 0; e < D / 32; ++e) {
-          const bf16x8 a = TR.cols(bs, 32 * t + 16 * u, e);
-          acc[e] = mfma32(a, hi, acc[e]);
-          acc[e] = mfma32(a, lo, acc[e]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 hi = pack_bf16x8(vt + 8 * u);
-#pragma unroll
-        for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(TR.cols(bs, 32 * t + 16 * u, e), hi, acc[e]);
-      }
+    for (int s = 0; s < D / 16; ++s) {
+      a0[s] = tr.rows(src, 0, s);
+      a1[s] = tr.rows(src, 32, s);
     }
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      c0 = mfma32(a0[s], bf[s], c0);
+      c1 = mfma32(a1[s], bf[s], c1);
+    }
+    pipeline_reads<D / 8>();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // S wave: S = Q K^T for both half tiles (two independent MFMA chains
-  // sharing each K fragment), P = exp(S - LSE) published through LDS, then
-  // dV^T += dO^T P.
-  auto compute_s = [&](const uint16_t* qs, const uint16_t* gs, const float* lse2s, int i0, bool active,
-                       bool need_mask) ATTN_INLINE {
-    float v[2][16];
-    if (active) {
-      f32x16 c0, c1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        c0[r] = 0.f;
-        c1[r] = 0.f;
-      }
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        c0 = mfma32(TR.rows(qs, 0, s), bf[s], c0);
-        c1 = mfma32(TR.rows(qs, 32, s), bf[s], c1);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * t + 8 * g + 4 * hh]);
-          f32x4 o;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float pv = fast_exp2(fmaf(t == 0 ? c0[4 * g + i] : c1[4 * g + i], sl2e, -l4[i]));
-            if (need_mask) {
-              const int q = i0 + 32 * t + 8 * g + 4 * hh + i;
-              pv = key > q ? 0.f : pv;
-            }
-            v[t][4 * g + i] = pv;
-            o[i] = pv;
-          }
-          *reinterpret_cast<f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]) = o;
-        }
-    }
-    __syncthreads();  // P of this tile is visible to the dP waves
-    if (active) {
-      accumulate(gs, v[0], 0);
-      accumulate(gs, v[1], 1);
-    }
-  };
-
-  // dP wave: dP = dO V^T accumulated onto -D (registers run over queries),
-  // so it ends with dP - D; after P arrives, dS = P * (dP - D), then
-  // dK^T += Q^T dS.
-  auto compute_dp = [&](const uint16_t* qs, const uint16_t* gs, const float* dsms, bool active) ATTN_INLINE {
-    float v[2][16];
-    if (active) {
-      f32x16 c0, c1;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dsms[8 * g + 4 * hh]);
-        const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dsms[32 + 8 * g + 4 * hh]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          c0[4 * g + i] = -d0[i];
-          c1[4 * g + i] = -d1[i];
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        c0 = mfma32(TR.rows(gs, 0, s), bf[s], c0);
-        c1 = mfma32(TR.rows(gs, 32, s), bf[s], c1);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        v[0][r] = c0[r];
-        v[1][r] = c1[r];
-      }
-    }
-    __syncthreads();  // P of this tile is ready
-    if (active) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 p4 = *reinterpret_cast<const f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[t][4 * g + i] *= p4[i];
-        }
-        accumulate(qs, v[t], t);
-      }
-    }
-  };
-
-  // The tile loop, once per role: each role's loop is its own region for the
-  // register allocator (the two roles together would not fit), and both run
-  // the same sequence of barriers.  A tile whose queries all precede this key
-  // group is skipped (causal); both waves of a pair decide alike, and every
-  // wave reaches the mid-tile barrier inside compute_s / compute_dp.
-  auto run = [&](auto&& compute) ATTN_INLINE {
-    issue(q0s, g0s, it0 * BQ);
-    publish(lse0s, dsm0s);
-    for (int it = it0; it < ntq; it += 2) {
-      if (it + 1 < ntq) issue(q1s, g1s, (it + 1) * BQ);
-      compute(q0s, g0s, lse0s, dsm0s, it * BQ);
-      publish(lse1s, dsm1s);
+  // Tile loop skeleton shared by both roles (same barriers in both): tile i
+  // lives in buffer b = (i - it0) mod 3.  body(b, i, mid) does the role's
+  // work on tile i and calls mid() exactly once, between its two halves.
+  auto run = [&](auto&& body) ATTN_INLINE {
+    auto step = [&](auto b, int i) ATTN_INLINE {
+      constexpr int B = decltype(b)::value;
+      if (i + 1 < ntq) load_small(i + 1);
+      body(b, i, [&]() ATTN_INLINE {
+        __syncthreads();  // P of tile i is published; reads of tile i - 1 are done
+        if (i + 2 < ntq) dma(i + 2, int_c<(B + 2) % 3>{});
+      });
+      if (i + 1 < ntq) store_small(int_c<(B + 1) % 3>{});
+      handover(i + 2 < ntq);
+    };
+    load_small(it0);
+    dma(it0, int_c<0>{});
+    if (it0 + 1 < ntq) dma(it0 + 1, int_c<1>{});
+    store_small(int_c<0>{});
+    handover(it0 + 1 < ntq);
+    for (int it = it0; it < ntq; it += 3) {
+      step(int_c<0>{}, it);
       if (it + 1 >= ntq) break;
-      if (it + 2 < ntq) issue(q0s, g0s, (it + 2) * BQ);
-      compute(q1s, g1s, lse1s, dsm1s, (it + 1) * BQ);
-      publish(lse0s, dsm0s);
+      step(int_c<1>{}, it + 1);
+      if (it + 2 >= ntq) break;
+      step(int_c<2>{}, it + 2);
     }
   };
+
   if (s_role) {
-    run([&](const uint16_t* qs, const uint16_t* gs, const float* lse2s, const float*, int i0) ATTN_INLINE {
-      compute_s(qs, gs, lse2s, i0, !CAUSAL || (i0 + BQ - 1 >= kw0), CAUSAL && (i0 < kw0 + 31));
+    // S wave: S = Q K^T, P = exp(S - LSE) published through LDS, then
+    // dV^T += dO^T P.
+    const TileReader<D, 0, GSHIFT> TR(lane);
+    run([&](auto b, int i, auto&& mid) ATTN_INLINE {
+      const bool act = active(i);
+      float v[2][16];
+      if (act) {
+        const float* lse2s = lse_at(b);
+        f32x16 c0, c1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          c0[r] = 0.f;
+          c1[r] = 0.f;
+        }
+        chains(TR, q_at(b), c0, c1);
+        const bool need_mask = CAUSAL && (i * BQ < kw0 + 31);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * t + 8 * g + 4 * hh]);
+            f32x4 o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              float pv = fast_exp2(fmaf(t == 0 ? c0[4 * g + k] : c1[4 * g + k], sl2e, -l4[k]));
+              if (need_mask) {
+                const int q = i * BQ + 32 * t + 8 * g + 4 * hh + k;
+                pv = key > q ? 0.f : pv;
+              }
+              v[t][4 * g + k] = pv;
+              o[k] = pv;
+            }
+            *reinterpret_cast<f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]) = o;
+          }
+      }
+      mid();
+      if (act) {
+        // hi terms always, lo terms only where the half tile needs them: the
+        // accumulators are only ever updated in place (no alternative paths
+        // that the register allocator would join with copies).
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 h[2] = {pack_bf16x8(v[t]), pack_bf16x8(v[t] + 8)};
+          const bool sp = needs_split(v[t]);
+          acc_plain(TR, g_at(b), h, t);
+          if (sp) {
+            const bf16x8 l[2] = {split_lo_bf16x8(v[t], h[0]), split_lo_bf16x8(v[t] + 8, h[1])};
+            acc_plain(TR, g_at(b), l, t);
+          }
+        }
+      }
     });
   } else {
-    run([&](const uint16_t* qs, const uint16_t* gs, const float*, const float* dsms, int i0) ATTN_INLINE {
-      compute_dp(qs, gs, dsms, !CAUSAL || (i0 + BQ - 1 >= kw0));
+    // dP wave: dP = dO V^T accumulated onto -D (registers run over queries),
+    // so it ends with dP - D; after P arrives, dS = P * (dP - D).  The dK^T
+    // += Q^T dS products of each half tile are deferred to the next tile's
+    // first half, with dS kept packed in registers (hi and, where the half
+    // tile needs the split, lo bf16 terms).
+    const TileReader<D, GSHIFT, 0> TR(lane);
+    bf16x8 dhi[2][2], dlo[2][2];
+    bool pend = false, spl0 = false, spl1 = false;
+    auto deferred = [&](const uint16_t* qs) ATTN_INLINE {
+      acc_plain(TR, qs, dhi[0], 0);
+      acc_plain(TR, qs, dhi[1], 1);
+      if (spl0) acc_plain(TR, qs, dlo[0], 0);
+      if (spl1) acc_plain(TR, qs, dlo[1], 1);
+    };
+    run([&](auto b, int i, auto&& mid) ATTN_INLINE {
+      constexpr int BP = (decltype(b)::value + 2) % 3;  // buffer of tile i - 1
+      if (pend) deferred(q_at(int_c<BP>{}));
+      const bool act = active(i);
+      f32x16 c0, c1;
+      if (act) {
+        const float* dsms = dsm_at(b);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dsms[8 * g + 4 * hh]);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dsms[32 + 8 * g + 4 * hh]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            c0[4 * g + k] = -d0[k];
+            c1[4 * g + k] = -d1[k];
+          }
+        }
+        chains(TR, g_at(b), c0, c1);
+      }
+      mid();
+      pend = act;
+      if (act) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float v[16];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[4 * g + k] = (t == 0 ? c0[4 * g + k] : c1[4 * g + k]) * p4[k];
+          }
+          const bool sp = needs_split(v);
+          (t == 0 ? spl0 : spl1) = sp;
+          dhi[t][0] = pack_bf16x8(v);
+          dhi[t][1] = pack_bf16x8(v + 8);
+          if (sp) {
+            dlo[t][0] = split_lo_bf16x8(v, dhi[t][0]);
+            dlo[t][1] = split_lo_bf16x8(v + 8, dhi[t][1]);
+          }
+        }
+      }
     });
+    // Deferred products of the last tile (no DMA is in flight any more).
+    if (pend) {
+      const int bl = (ntq - 1 - it0) % 3;
+      deferred(bl == 0 ? q_at(int_c<0>{}) : bl == 1 ? q_at(int_c<1>{}) : q_at(int_c<2>{}));
+    }
   }
 
   if (key < n) {

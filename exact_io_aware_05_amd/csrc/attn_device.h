@@ -94,6 +94,19 @@ __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8&
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
+// The lo term of split_bf16x8 for a given hi = pack_bf16x8(x).
+__device__ __forceinline__ bf16x8 split_lo_bf16x8(const float* x, bf16x8 hi) {
+  const u32x4 h = __builtin_bit_cast(u32x4, hi);
+  u32x4 l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float r0 = x[2 * i] - __uint_as_float(h[i] << 16);
+    const float r1 = x[2 * i + 1] - __uint_as_float(h[i] & 0xFFFF0000u);
+    l[i] = pack_bf16x2(r0, r1);
+  }
+  return __builtin_bit_cast(bf16x8, l);
+}
+
 // Low 16 bits of a and b packed (a low), and high 16 bits of a and b packed.
 __device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

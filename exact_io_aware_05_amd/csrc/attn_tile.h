@@ -43,6 +43,14 @@ __device__ __forceinline__ constexpr uint32_t tile_off(int row, int c) {
 // included); lgkm and export counters are left unconstrained.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order), lgkm and export unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // DMA rows [row0, row0 + 64) of a [n, D] bf16 matrix (buffer `rs`) into the
 // LDS tile at `lds`.  The NW waves of the workgroup split the 64 rows.
 template <int D, int NW>
@@ -50,6 +58,10 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* ld
   constexpr int CPR = D / 8;      // 16-byte chunks per row
   constexpr int IPW = CPR / NW;   // 1 KiB loads per wave
   static_assert(IPW >= 1 && IPW * NW == CPR, "waves must split the tile evenly");
+  // The tile's byte offset goes through readfirstlane: opaque to loop
+  // strength reduction, which would otherwise keep one address vector per
+  // load and buffer alive across the tile loop.
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (D * 2));
 #pragma unroll
   for (int r = 0; r < IPW; ++r) {
     const int k = w * IPW + r;
@@ -57,7 +69,7 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* ld
     const int row = p / CPR, cp = p % CPR;
     const int c = cp ^ tile_swz<D>(row);  // global chunk that belongs there
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(lds + 512 * k), 16,
-                                             (uint32_t)(row0 + row) * (D * 2) + 16 * c, 0, 0, 0);
+                                             base + (uint32_t)(row * (D * 2) + 16 * c), 0, 0, 0);
   }
 }
 
@@ -77,7 +89,11 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* ld
 //    i element i % 4 of the 8-byte piece addressed by lane 4s + i/4, so lane
 //    j = 4s + c addresses row (4h + s) and features 4c .. 4c+3 of its group's
 //    16-feature slice.
-template <int D>
+// An LDS read reaches at most 64 KiB past its address register.  A kernel
+// whose tiles extend beyond that gives the reader byte shifts RS (row reads)
+// and CS (transposed reads): the shift moves into the per-lane bases (hidden
+// from the compiler, so it is not folded back) and out of the immediate.
+template <int D, int RS = 0, int CS = 0>
 struct TileReader {
   static constexpr int NS = D / 16;  // row fragments per row
   static constexpr int NE = D / 32;  // transposed fragments per 32 features
@@ -99,15 +115,31 @@ struct TileReader {
         const int r = r0 + 8 * k;
         col_base[e][k] = (uint32_t)(r * (D * 2) + 16 * ((4 * e + z) ^ tile_swz<D>(r)) + 8 * (i16 & 1));
       }
+    if constexpr (RS != 0) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        row_base[s] += RS;
+        asm("" : "+v"(row_base[s]));
+      }
+    }
+    if constexpr (CS != 0) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          col_base[e][k] += CS;
+          asm("" : "+v"(col_base[e][k]));
+        }
+    }
   }
 
   __device__ __forceinline__ bf16x8 rows(const uint16_t* lds, int rbase, int s) const {
-    const char* p = reinterpret_cast<const char*>(lds) + row_base[s] + rbase * (D * 2);
+    const char* p = reinterpret_cast<const char*>(lds) + (rbase * (D * 2) - RS) + row_base[s];
     return *reinterpret_cast<const bf16x8*>(p);
   }
 
   __device__ __forceinline__ bf16x8 cols(const uint16_t* lds, int rbase, int e) const {
-    const char* p = reinterpret_cast<const char*>(lds) + rbase * (D * 2);
+    const char* p = reinterpret_cast<const char*>(lds) + (rbase * (D * 2) - CS);
     const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)(p + col_base[e][0]));
     const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ATTN_LDS s16x4*)(p + col_base[e][1]));
     u32x4 u;
