@@ -483,14 +483,32 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
       }
 
       float ds[16];
+      if constexpr (CAUSAL) {
+        // Exponent arguments; entries above the diagonal (diagonal tiles
+        // only, a wave-uniform branch) become -inf, whose exp2 is 0.  Keys
+        // past n lie above the diagonal of every row that is written.
+        float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = fast_exp2(fmaf(sacc[r], sl2e, -l2));
+        for (int r = 0; r < 16; ++r) x[r] = fmaf(sacc[r], sl2e, -l2);
         if (need_mask) {
-          const int kj = j0 + 32 * t + crow(r, hh);
-          pv = (kj >= n || (CAUSAL && kj > qrow)) ? 0.f : pv;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kj = j0 + 32 * t + crow(r, hh);
+            x[r] = kj > qrow ? -INFINITY : x[r];
+          }
         }
-        ds[r] = pv * (pacc[r] - dq_d);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(x[r]) * (pacc[r] - dq_d);
+      } else {
+        // Full mask: only keys past n (ragged last tile) are masked; the
+        // compiler turns this into selects, which keeps the loop within the
+        // register file at two waves per SIMD.
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = fast_exp2(fmaf(sacc[r], sl2e, -l2));
+          if (need_mask) pv = (j0 + 32 * t + crow(r, hh) >= n) ? 0.f : pv;
+          ds[r] = pv * (pacc[r] - dq_d);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
