@@ -25,6 +25,9 @@ Modules:
 * :mod:`oracle.online` -- the pages' tiled online-softmax forward, kept only
   to pin the definition (tiled == one-shot) and to replay the pages' worked
   examples step by step.
+* :mod:`oracle.blocksparse` -- the same definition under a block mask (the
+  block-sparse variant named in "Experiments & Results" on the Paper Notes
+  page), with the conventions for rows that allow no key.
 
 Every function here is pinned by ``tests/test_oracle*.py`` against page-printed
 values, closed forms, invariants, finite differences and a library autograd;
