@@ -11,6 +11,8 @@ Entry points carry the C names:
 * :func:`attn_bwd` (q, k, v, o, do, lse, causal, scale) -> (dq, dk, dv)
 * :func:`attn_bwd_dsum`, :func:`attn_bwd_dkdv`, :func:`attn_bwd_dq` -- the
   three phases of the backward pass, for use on separate streams or timing
+* :func:`attn_fwd_blocksparse`, :func:`attn_bwd_blocksparse` -- the same
+  with a block mask over 128 x 128 blocks of the score matrix
 * :func:`attn_bwd_workspace_bytes`, :func:`attn_status_string`
 * :func:`lib` -- the raw ``ctypes.CDLL``.
 """
@@ -25,6 +27,9 @@ __all__ = [
     "attn_bwd_dsum",
     "attn_bwd_dkdv",
     "attn_bwd_dq",
+    "attn_fwd_blocksparse",
+    "attn_bwd_blocksparse",
+    "SPARSE_BLOCK",
     "attn_bwd_workspace_bytes",
     "attn_status_string",
     "lib",
@@ -38,6 +43,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so"
 
 ATTN_BF16 = 0
 ATTN_FP32 = 1
+SPARSE_BLOCK = 128  # ATTN_SPARSE_BLOCK: rows per block of the block-sparse mask
 
 _lib = None
 
@@ -75,6 +81,11 @@ def lib():
     L.attn_bwd_dkdv.restype = i32
     L.attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp]
     L.attn_bwd_dq.restype = i32
+    L.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp, i64, vp]
+    L.attn_fwd_blocksparse.restype = i32
+    L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp,
+                                       i64, vp, ctypes.c_size_t, vp]
+    L.attn_bwd_blocksparse.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -234,3 +245,79 @@ def attn_bwd_dq(q, k, v, do, lse, dsum, causal=False, scale=None, dq=None):
     if st != 0:
         raise AttnError(st, "attn_bwd_dq")
     return dq
+
+
+def _block_mask(mask, B, H, N, device):
+    """Validate a block mask tensor; returns (tensor, head stride in bytes).
+
+    Accepted: uint8 or bool, contiguous, on ``device``, shaped [nb, nb] (one
+    mask for every head), [B, H, nb, nb] or [B * H, nb, nb], with
+    nb = ceil(N / 128).
+    """
+    torch = _torch()
+    nb = (N + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    if mask.dtype not in (torch.uint8, torch.bool):
+        raise TypeError(f"block_mask: dtype {mask.dtype}; use torch.uint8 or torch.bool")
+    if mask.device != device or not mask.is_contiguous():
+        raise ValueError("block_mask must be a contiguous tensor on the inputs' device")
+    if tuple(mask.shape) == (nb, nb):
+        return mask, 0
+    if tuple(mask.shape) in ((B, H, nb, nb), (B * H, nb, nb)):
+        return mask, nb * nb
+    raise ValueError(f"block_mask: shape {tuple(mask.shape)}; expected ({nb}, {nb}), "
+                     f"({B}, {H}, {nb}, {nb}) or ({B * H}, {nb}, {nb})")
+
+
+def attn_fwd_blocksparse(q, k, v, block_mask, causal=False, scale=None, out=None, lse=None):
+    """Block-sparse forward: query i attends key j only where the 128 x 128
+    block holding (i, j) is nonzero in ``block_mask`` (and j <= i if
+    ``causal``).  Rows with no allowed key get O = 0, LSE = -inf.  bf16 only.
+    Returns (o, lse)."""
+    torch = _torch()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v)], q.shape, q.dtype, q.device)
+    mask, stride = _block_mask(block_mask, B, H, N, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check([("out", out)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    st = lib().attn_fwd_blocksparse(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, _dtype_code(q),
+        int(bool(causal)), float(scale), mask.data_ptr(), stride, _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_fwd_blocksparse")
+    return out, lse
+
+
+def attn_bwd_blocksparse(q, k, v, o, do, lse, block_mask, causal=False, scale=None, workspace=None, grads=None):
+    """Block-sparse backward (same mask and causal flag as the forward);
+    returns (dq, dk, dv)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v), ("o", o), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    mask, stride = _block_mask(block_mask, B, H, N, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    _check([("dq", dq), ("dk", dk), ("dv", dv)], q.shape, q.dtype, q.device)
+    st = lib().attn_bwd_blocksparse(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, code, int(bool(causal)), float(scale),
+        mask.data_ptr(), stride, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_bwd_blocksparse")
+    return dq, dk, dv

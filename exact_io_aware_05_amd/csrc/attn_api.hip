@@ -23,6 +23,17 @@ int check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Block-sparse mask arguments (shape already validated): a mask, bf16, and a
+// head stride of 0 or at least nb * nb whose last head stays addressable.
+int check_mask(const uint8_t* mask, int64_t stride, int64_t B, int64_t H, int64_t N, int dtype) {
+  if (!mask) return ATTN_E_NULL;
+  if (dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  const int64_t nb = (N + ATTN_SPARSE_BLOCK - 1) / ATTN_SPARSE_BLOCK;
+  if (stride < 0 || (stride != 0 && stride < nb * nb)) return ATTN_E_SHAPE;
+  if (stride != 0 && B * H - 1 > (INT64_MAX - nb * nb) / stride) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
 attn::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                        const float* lse, void* dq, void* dk, void* dv, float* dsum, int64_t B, int64_t H, int64_t N,
                        int64_t d, int causal, float scale, void* stream) {
@@ -54,8 +65,8 @@ const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_E_NULL: return "a required pointer is NULL";
-    case ATTN_E_SHAPE: return "invalid shape (B, H, N must be >= 1 and within size limits)";
-    case ATTN_E_UNSUPPORTED: return "unsupported head dimension (64 or 128) or dtype (bf16 or fp32)";
+    case ATTN_E_SHAPE: return "invalid shape (B, H, N must be >= 1 and within size limits) or block-mask stride";
+    case ATTN_E_UNSUPPORTED: return "unsupported head dimension (64 or 128) or dtype (bf16 or fp32; block-sparse: bf16)";
     case ATTN_E_SCALE: return "scale must be finite";
     case ATTN_E_WORKSPACE: return "workspace missing or too small";
     case ATTN_E_HIP: return "HIP kernel launch failed";
@@ -142,6 +153,55 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if (attn::bwd_dsum(a, bf16) != hipSuccess) return ATTN_E_HIP;
   if ((bf16 ? attn::bwd_bf16_dkdv(a) : attn::bwd_f32_dkdv(a)) != hipSuccess) return ATTN_E_HIP;
   if ((bf16 ? attn::bwd_bf16_dq(a) : attn::bwd_f32_dq(a)) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
+}
+
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                         int64_t N, int64_t d, int dtype, int causal, float scale, const uint8_t* block_mask,
+                         int64_t mask_head_stride, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  st = check_mask(block_mask, mask_head_stride, B, H, N, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = B * H;
+  a.n = N;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  a.bmask = block_mask;
+  a.mask_stride = mask_head_stride;
+  return attn::fwd_bf16(a) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                         int dtype, int causal, float scale, const uint8_t* block_mask, int64_t mask_head_stride,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  st = check_mask(block_mask, mask_head_stride, B, H, N, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, dtype) ||
+      ((uintptr_t)workspace & 255) != 0)
+    return ATTN_E_WORKSPACE;
+  attn::BwdArgs a =
+      make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
+  a.bmask = block_mask;
+  a.mask_stride = mask_head_stride;
+  if (attn::bwd_dsum(a, true) != hipSuccess) return ATTN_E_HIP;
+  if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
+  if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
 }
 

@@ -94,7 +94,7 @@ __device__ __forceinline__ void pipeline_reads2() {
 template <int N>
 using int_c = std::integral_constant<int, N>;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ K,
                                                         const uint16_t* __restrict__ V,
@@ -102,7 +102,8 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
                                                         const float* __restrict__ LSE,
                                                         const float* __restrict__ Dsum,
                                                         uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                                                        int n, int nkb, int total, float scale, float sl2e) {
+                                                        int n, int nkb, int total, float scale, float sl2e,
+                                                        const uint8_t* __restrict__ bmask, long long mask_stride) {
   constexpr int NW = 8, BKV = 128, BQ = 64;
   constexpr int TB = BQ * D * 2;  // bytes per 64-row tile
   constexpr int IPW = (D / 8) / NW;  // DMA loads per wave per tile
@@ -163,9 +164,22 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 
   const int ntq = (n + BQ - 1) / BQ;
   const int it0 = CAUSAL ? (k0 / BQ) : 0;
+  // Block-sparse: a query tile is wanted when its mask block (a 64-row tile
+  // is half of a 128-row block) may attend this key block (a workgroup's 128
+  // keys are one mask block column).  Unwanted tiles are neither fetched nor
+  // computed; the loop still steps through them, so the barriers stay
+  // uniform.
+  const uint8_t* mcol = SPARSE ? bmask + (size_t)bh * mask_stride + kb : nullptr;
+  const int nbq = (n + kSparseBlock - 1) / kSparseBlock;
+  auto want = [&](int i) ATTN_INLINE {
+    if constexpr (SPARSE)
+      return __builtin_amdgcn_readfirstlane(mcol[(size_t)(i >> 1) * nbq]) != 0;
+    else
+      return true;
+  };
   // A tile whose queries all precede this key group is skipped (causal);
   // both waves of a pair decide alike.
-  auto active = [&](int i) ATTN_INLINE { return !CAUSAL || (i * BQ + BQ - 1 >= kw0); };
+  auto active = [&](int i) ATTN_INLINE { return (!CAUSAL || (i * BQ + BQ - 1 >= kw0)) && want(i); };
 
   // Query rows past n load as zero (Q, dO, LSE, D), so they contribute
   // nothing: P = 1 is finite and multiplies dO = 0 and dS = 0.
@@ -250,19 +264,24 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   auto run = [&](auto&& body) ATTN_INLINE {
     auto step = [&](auto b, int i) ATTN_INLINE {
       constexpr int B = decltype(b)::value;
-      if (i + 1 < ntq) load_small(i + 1);
+      const bool w1 = i + 1 < ntq && want(i + 1);
+      const bool w2 = i + 2 < ntq && want(i + 2);
+      if (w1) load_small(i + 1);
       body(b, i, [&]() ATTN_INLINE {
         __syncthreads();  // P of tile i is published; reads of tile i - 1 are done
-        if (i + 2 < ntq) dma(i + 2, int_c<(B + 2) % 3>{});
+        if (w2) dma(i + 2, int_c<(B + 2) % 3>{});
       });
-      if (i + 1 < ntq) store_small(int_c<(B + 1) % 3>{});
-      handover(i + 2 < ntq);
+      if (w1) store_small(int_c<(B + 1) % 3>{});
+      handover(w2);
     };
-    load_small(it0);
-    dma(it0, int_c<0>{});
-    if (it0 + 1 < ntq) dma(it0 + 1, int_c<1>{});
-    store_small(int_c<0>{});
-    handover(it0 + 1 < ntq);
+    const bool w0 = want(it0), w1 = it0 + 1 < ntq && want(it0 + 1);
+    if (w0) {
+      load_small(it0);
+      dma(it0, int_c<0>{});
+    }
+    if (w1) dma(it0 + 1, int_c<1>{});
+    if (w0) store_small(int_c<0>{});
+    handover(w1);
     for (int it = it0; it < ntq; it += 3) {
       step(int_c<0>{}, it);
       if (it + 1 >= ntq) break;
@@ -341,7 +360,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
       if (spl1) acc_plain(TR, qs, dlo[1], 1);
     };
     run([&](auto b, int i, auto&& mid) ATTN_INLINE {
-      constexpr int BP = (decltype(b)::value + 2) % 3;  // buffer of tile i - 1
+      constexpr int BP = (decltype(b)::value + 2) % 3;  // buffer of the previous tile
       if (pend) deferred(q_at(int_c<BP>{}));
       const bool act = active(i);
       f32x16 c0, c1;
@@ -407,7 +426,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // dQ: query-stationary
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __restrict__ Q,
                                                            const uint16_t* __restrict__ K,
                                                            const uint16_t* __restrict__ V,
@@ -415,7 +434,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
                                                            const float* __restrict__ LSE,
                                                            const float* __restrict__ Dsum,
                                                            uint16_t* __restrict__ dQ, int n, int nqb, int total,
-                                                           float scale, float sl2e) {
+                                                           float scale, float sl2e,
+                                                           const uint8_t* __restrict__ bmask, long long mask_stride,
+                                                           int nb) {
   constexpr int BR = NW * 32, BC = 64;
 
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[BC * D];
@@ -461,9 +482,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   const int kend = CAUSAL ? min(n, q0 + BR) : n;
   const int ntiles = (kend + BC - 1) / BC;
 
+  // Block-sparse: this wave's 32 rows lie in one mask block row.
+  const uint8_t* mrow_w = SPARSE ? bmask + (size_t)bh * mask_stride + (size_t)(wq0 / kSparseBlock) * nb : nullptr;
+
   auto compute = [&](const uint16_t* ks, const uint16_t* vs, int j0) {
     const bool active = !CAUSAL || (j0 <= wq0 + 31);
     if (!active) return;
+    if constexpr (SPARSE) {
+      if (wq0 >= n || __builtin_amdgcn_readfirstlane(mrow_w[j0 / kSparseBlock]) == 0) return;
+    }
     const bool need_mask = (j0 + BC > n) || (CAUSAL && j0 + BC - 1 > wq0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -520,6 +547,50 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
     }
   };
 
+  if constexpr (SPARSE) {
+    // Key tiles that some query block of this workgroup may attend (BR / 128
+    // mask block rows; a 64-key tile is half of a mask block), in order.
+    constexpr int QBLK = BR / kSparseBlock;
+    static_assert(QBLK * kSparseBlock == BR, "workgroups cover whole mask block rows");
+    const uint8_t* mrow = bmask + (size_t)bh * mask_stride + (size_t)(q0 / kSparseBlock) * nb;
+    const int nrows = min(QBLK, nb - q0 / kSparseBlock);
+    auto wanted = [&](int j) ATTN_INLINE {
+      bool any = false;
+      for (int r = 0; r < nrows; ++r)
+        any = any || __builtin_amdgcn_readfirstlane(mrow[(size_t)r * nb + (j >> 1)]) != 0;
+      return any;
+    };
+    auto next = [&](int j) ATTN_INLINE {
+      while (j < ntiles && !wanted(j)) ++j;
+      return j;
+    };
+    int jc = next(0);
+    if (jc < ntiles) {
+      dma_tile<D, NW>(rk, k0s, jc * BC, w, lane);
+      dma_tile<D, NW>(rv, v0s, jc * BC, w, lane);
+      wait_vmem();
+      __syncthreads();
+    }
+    while (jc < ntiles) {
+      const int jn = next(jc + 1);
+      if (jn < ntiles) {
+        dma_tile<D, NW>(rk, k1s, jn * BC, w, lane);
+        dma_tile<D, NW>(rv, v1s, jn * BC, w, lane);
+      }
+      compute(k0s, v0s, jc * BC);
+      wait_vmem();
+      __syncthreads();
+      if (jn >= ntiles) break;
+      jc = next(jn + 1);
+      if (jc < ntiles) {
+        dma_tile<D, NW>(rk, k0s, jc * BC, w, lane);
+        dma_tile<D, NW>(rv, v0s, jc * BC, w, lane);
+      }
+      compute(k1s, v1s, jn * BC);
+      wait_vmem();
+      __syncthreads();
+    }
+  } else {
   dma_tile<D, NW>(rk, k0s, 0, w, lane);
   dma_tile<D, NW>(rv, v0s, 0, w, lane);
   wait_vmem();
@@ -542,6 +613,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
     wait_vmem();
     __syncthreads();
   }
+  }
 
   if (qrow < n) {
     uint16_t* drow = dQ + head + (size_t)qrow * D;
@@ -557,14 +629,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_dkdv(const BwdArgs& a) {
   const int n = (int)a.n;
   const int nkb = (n + 127) / 128;
   const int total = (int)(a.bh * nkb);
-  hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL>), dim3(total), dim3(512), 0, a.stream, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
-                     (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e);
+  hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, SPARSE>), dim3(total), dim3(512), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                     a.lse, a.dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e,
+                     a.bmask, (long long)a.mask_stride);
   return hipGetLastError();
 }
 
@@ -572,28 +645,36 @@ hipError_t launch_dkdv(const BwdArgs& a) {
 #define ATTN_DQ_NW128 8  // waves per dQ workgroup at d = 128 (tuning knob)
 #endif
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_dq(const BwdArgs& a) {
   constexpr int NW = D == 128 ? ATTN_DQ_NW128 : 4;
   const int n = (int)a.n;
   const int nqb = (n + NW * 32 - 1) / (NW * 32);
   const int total = (int)(a.bh * nqb);
-  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL>), dim3(total), dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
-                     (uint16_t*)a.dq, n, nqb, total, a.scale, a.scale * kLog2e);
+  const int nb = (n + kSparseBlock - 1) / kSparseBlock;
+  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE>), dim3(total), dim3(NW * 64), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
+                     a.lse, a.dsum, (uint16_t*)a.dq, n, nqb, total, a.scale, a.scale * kLog2e, a.bmask,
+                     (long long)a.mask_stride, nb);
   return hipGetLastError();
+}
+
+template <bool SPARSE>
+hipError_t dkdv_t(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_dkdv<64, true, SPARSE>(a) : launch_dkdv<64, false, SPARSE>(a);
+  return a.causal ? launch_dkdv<128, true, SPARSE>(a) : launch_dkdv<128, false, SPARSE>(a);
+}
+
+template <bool SPARSE>
+hipError_t dq_t(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_dq<64, true, SPARSE>(a) : launch_dq<64, false, SPARSE>(a);
+  return a.causal ? launch_dq<128, true, SPARSE>(a) : launch_dq<128, false, SPARSE>(a);
 }
 
 }  // namespace
 
-hipError_t bwd_bf16_dkdv(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_dkdv<64, true>(a) : launch_dkdv<64, false>(a);
-  return a.causal ? launch_dkdv<128, true>(a) : launch_dkdv<128, false>(a);
-}
+hipError_t bwd_bf16_dkdv(const BwdArgs& a) { return a.bmask ? dkdv_t<true>(a) : dkdv_t<false>(a); }
 
-hipError_t bwd_bf16_dq(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_dq<64, true>(a) : launch_dq<64, false>(a);
-  return a.causal ? launch_dq<128, true>(a) : launch_dq<128, false>(a);
-}
+hipError_t bwd_bf16_dq(const BwdArgs& a) { return a.bmask ? dq_t<true>(a) : dq_t<false>(a); }
 
 }  // namespace attn

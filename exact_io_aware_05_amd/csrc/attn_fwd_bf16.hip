@@ -39,13 +39,15 @@
 
 namespace attn {
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
                                                               const uint16_t* __restrict__ K,
                                                               const uint16_t* __restrict__ V,
                                                               uint16_t* __restrict__ O,
                                                               float* __restrict__ LSE, int n, int nqb,
-                                                              int total, float c, uint32_t qsign) {
+                                                              int total, float c, uint32_t qsign,
+                                                              const uint8_t* __restrict__ bmask,
+                                                              long long mask_stride, int nb) {
   constexpr int BC = 64;                // keys per tile
   constexpr int BR = NW * 32;           // query rows per workgroup
   constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
@@ -170,6 +172,43 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
           oacc[e] = mfma32(TR.cols(vb, 32 * t + 16 * u, e), pf[t][u], oacc[e]);
   };
 
+  if constexpr (SPARSE) {
+    // Block-sparse: only the key tiles of the blocks this query block may
+    // attend are fetched and computed (a workgroup's 128 rows are exactly one
+    // mask block row; a 64-key tile is half of a mask block).
+    static_assert(BR == kSparseBlock, "one workgroup per mask block row");
+    const uint8_t* mrow = bmask + (size_t)bh * mask_stride + (size_t)qb * nb;
+    auto next = [&](int j) ATTN_INLINE {
+      while (j < ntiles && __builtin_amdgcn_readfirstlane(mrow[j >> 1]) == 0) ++j;
+      return j;
+    };
+    int jc = next(0);
+    if (jc < ntiles) {
+      dma_tile<D, NW>(rk, k0s, jc * BC, w, lane);
+      dma_tile<D, NW>(rv, v0s, jc * BC, w, lane);
+      wait_vmem();
+      __syncthreads();
+    }
+    while (jc < ntiles) {
+      const int jn = next(jc + 1);
+      if (jn < ntiles) {
+        dma_tile<D, NW>(rk, k1s, jn * BC, w, lane);
+        dma_tile<D, NW>(rv, v1s, jn * BC, w, lane);
+      }
+      compute(k0s, v0s, jc * BC);
+      wait_vmem();
+      __syncthreads();
+      if (jn >= ntiles) break;
+      jc = next(jn + 1);
+      if (jc < ntiles) {
+        dma_tile<D, NW>(rk, k0s, jc * BC, w, lane);
+        dma_tile<D, NW>(rv, v0s, jc * BC, w, lane);
+      }
+      compute(k1s, v1s, jn * BC);
+      wait_vmem();
+      __syncthreads();
+    }
+  } else {
   dma_tile<D, NW>(rk, k0s, 0, w, lane);
   dma_tile<D, NW>(rv, v0s, 0, w, lane);
   wait_vmem();
@@ -194,10 +233,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
     wait_vmem();
     __syncthreads();
   }
+  }
 
   // Epilogue: O = acc / l (bf16, nearest-even), LSE = (m c + log2 l) ln 2.
+  // Block-sparse rows that may attend no key have l = 0: O = 0 and
+  // LSE = -inf (m stayed -inf).
   const float ltot = half_sum(lsum);
-  const float inv = 1.0f / ltot;
+  const float inv = (SPARSE && ltot == 0.f) ? 0.f : 1.0f / ltot;
   if (qrow < n) {
     uint16_t* orow = O + head + (size_t)qrow * D;
 #pragma unroll
@@ -213,7 +255,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   }
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, bool SPARSE>
 static hipError_t launch_fwd(const FwdArgs& a) {
   constexpr int BR = NW * 32;
   const int nqb = (int)((a.n + BR - 1) / BR);
@@ -224,15 +266,19 @@ static hipError_t launch_fwd(const FwdArgs& a) {
   float c = fabsf(a.scale) * kLog2e;
   if (c < 1e-30f) c = 1e-30f;
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL>), dim3(total), dim3(NW * 64), 0, a.stream,
+  const int nb = (int)((a.n + kSparseBlock - 1) / kSparseBlock);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE>), dim3(total), dim3(NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     (int)a.n, nqb, total, c, qsign);
+                     (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb);
   return hipGetLastError();
 }
 
-hipError_t fwd_bf16(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_fwd<64, 4, true>(a) : launch_fwd<64, 4, false>(a);
-  return a.causal ? launch_fwd<128, 4, true>(a) : launch_fwd<128, 4, false>(a);
+template <bool SPARSE>
+static hipError_t fwd_bf16_t(const FwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_fwd<64, 4, true, SPARSE>(a) : launch_fwd<64, 4, false, SPARSE>(a);
+  return a.causal ? launch_fwd<128, 4, true, SPARSE>(a) : launch_fwd<128, 4, false, SPARSE>(a);
 }
+
+hipError_t fwd_bf16(const FwdArgs& a) { return a.bmask ? fwd_bf16_t<true>(a) : fwd_bf16_t<false>(a); }
 
 }  // namespace attn

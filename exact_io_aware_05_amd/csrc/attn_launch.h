@@ -20,6 +20,11 @@ struct FwdArgs {
   bool causal;
   float scale;
   hipStream_t stream;
+  // Block-sparse variant (bf16 only): uint8 mask over 128 x 128 blocks of the
+  // score matrix, [ceil(n / 128)]^2 per head, heads mask_stride bytes apart
+  // (0: one mask for every head).  nullptr: dense.
+  const uint8_t* bmask = nullptr;
+  int64_t mask_stride = 0;
 };
 
 struct BwdArgs {
@@ -39,7 +44,12 @@ struct BwdArgs {
   bool causal;
   float scale;
   hipStream_t stream;
+  const uint8_t* bmask = nullptr;  // as in FwdArgs
+  int64_t mask_stride = 0;
 };
+
+// Block size of the block-sparse mask (query and key rows per block).
+constexpr int kSparseBlock = 128;
 
 hipError_t fwd_bf16(const FwdArgs& a);
 hipError_t fwd_f32(const FwdArgs& a);

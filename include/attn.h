@@ -144,6 +144,49 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                 int64_t H, int64_t N, int64_t d, int dtype, int causal,
                 float scale, void* stream);
 
+/*
+ * Block-sparse attention: the block-sparse variant of the method that the
+ * page "Paper Notes: FlashAttention" reports in "Experiments & Results"
+ * (faster than dense FlashAttention in proportion to the sparsity).  The
+ * pages give no further detail; here the score matrix of each head is cut
+ * into ATTN_SPARSE_BLOCK x ATTN_SPARSE_BLOCK blocks (query block, key block)
+ * and a caller-supplied mask says which blocks are computed.  Query i may
+ * attend key j only when the block holding (i, j) is nonzero in the mask
+ * (and, with `causal`, also j <= i); masked scores count as -inf, so the
+ * result is the exact softmax over each row's allowed keys.  Masked blocks
+ * are skipped, not computed.  A row with no allowed key gets O = 0,
+ * LSE = -inf and dQ = 0, and contributes nothing to dK and dV.
+ *
+ *   block_mask       : device memory, uint8, [nb, nb] per head, row-major
+ *                      (query block, key block), nb = ceil(N / 128);
+ *                      nonzero = computed.  Read only; must not change
+ *                      while the call runs.
+ *   mask_head_stride : bytes between the masks of consecutive heads, in
+ *                      b * H + h order; 0 = one mask for every head, else at
+ *                      least nb * nb.
+ *
+ * Other arguments, layouts, ownership and errors as for attn_fwd / attn_bwd;
+ * attn_bwd_blocksparse must get the mask and causal flag given to
+ * attn_fwd_blocksparse, and the same workspace size as attn_bwd.  bf16 only
+ * (ATTN_FP32 returns ATTN_E_UNSUPPORTED); a NULL mask is ATTN_E_NULL, a
+ * stride out of range ATTN_E_SHAPE.  Deterministic, like the dense calls.
+ */
+#define ATTN_SPARSE_BLOCK 128
+
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
+                         float* lse, int64_t B, int64_t H, int64_t N,
+                         int64_t d, int dtype, int causal, float scale,
+                         const uint8_t* block_mask, int64_t mask_head_stride,
+                         void* stream);
+
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                         int64_t N, int64_t d, int dtype, int causal,
+                         float scale, const uint8_t* block_mask,
+                         int64_t mask_head_stride, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);
 

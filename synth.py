@@ -65,6 +65,14 @@ def qkvdo(seed, shape, dtype="bf16", with_do=True):
     return out
 
 
+def block_mask(seed, nb, density, heads=None):
+    """Seeded uint8 block mask [nb, nb] (or [heads, nb, nb]) with each block
+    kept with probability ``density`` (numpy PCG64, uniform draws)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (nb, nb) if heads is None else (heads, nb, nb)
+    return (rng.random(shape) < density).astype(np.uint8)
+
+
 class Workload:
     """One named attention workload: shape, dtype, mask and seed."""
 

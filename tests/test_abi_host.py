@@ -28,11 +28,13 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == [
         "attn_bwd",
+        "attn_bwd_blocksparse",
         "attn_bwd_dkdv",
         "attn_bwd_dq",
         "attn_bwd_dsum",
         "attn_bwd_workspace_bytes",
         "attn_fwd",
+        "attn_fwd_blocksparse",
         "attn_status_string",
     ]
 
@@ -118,6 +120,36 @@ def test_backward_phase_validation():
         assert L.attn_bwd_dq(*ptrs, 1, 1, 16, 64, 0, 1, 0.1, None) == -1
     assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 0, 64, 0, 1, 0.1, None) == -2
     assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 16, 64, 0, 1, float("inf"), None) == -4
+
+
+def test_blocksparse_argument_validation():
+    E, L = _lib()
+
+    def fwd(ptrs=(FAKE,) * 5, B=2, H=3, N=300, d=64, dtype=0, mask=FAKE, stride=0, scale=0.1):
+        return L.attn_fwd_blocksparse(*ptrs, B, H, N, d, dtype, 0, scale, mask, stride, None)
+
+    def bwd(ptrs=(FAKE,) * 9, B=2, H=3, N=300, d=64, dtype=0, mask=FAKE, stride=0, ws=FAKE * 256, wsb=None):
+        if wsb is None:
+            wsb = L.attn_bwd_workspace_bytes(B, H, N, d, 0)
+        return L.attn_bwd_blocksparse(*ptrs, B, H, N, d, dtype, 1, 0.1, mask, stride, ws, wsb, None)
+
+    nb = 3  # ceil(300 / 128)
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert fwd(ptrs=ptrs) == -1
+    for i in range(9):
+        ptrs = [FAKE] * 9
+        ptrs[i] = None
+        assert bwd(ptrs=ptrs) == -1
+    assert fwd(mask=None) == -1 and bwd(mask=None) == -1
+    assert fwd(dtype=1) == -3 and bwd(dtype=1) == -3  # bf16 only
+    assert fwd(d=96) == -3 and fwd(N=0) == -2
+    assert fwd(stride=-1) == -2 and bwd(stride=nb * nb - 1) == -2
+    assert fwd(stride=2**62) == -2  # last head's mask not addressable
+    assert fwd(scale=float("nan")) == -4
+    assert bwd(ws=None) == -5 and bwd(ws=FAKE * 256 + 8) == -5
+    assert E.SPARSE_BLOCK == 128
 
 
 def test_workspace_size():

@@ -1,0 +1,173 @@
+"""GPU parity of the block-sparse forward and backward (through the C ABI)
+against the block-sparse float64 oracle (oracle/blocksparse.py), plus exact
+agreement with the dense path where the mask is all ones or implied by the
+causal mask."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import blocksparse as BS
+from tests.gpu_util import assert_close, download, upload
+
+pytestmark = [pytest.mark.gpu]
+
+BLOCK = 128
+
+
+def _api():
+    import exact_io_aware_05_amd as E
+
+    E.lib()
+    return E
+
+
+def _announce(*a):
+    print("[case]", *a, flush=True)
+
+
+def _gpu(inp, mask, causal, scale):
+    E = _api()
+    q, k, v, do = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v", "do"))
+    m = torch.from_numpy(np.ascontiguousarray(mask)).cuda()
+    o, lse = E.attn_fwd_blocksparse(q, k, v, m, causal=causal, scale=scale)
+    dq, dk, dv = E.attn_bwd_blocksparse(q, k, v, o, do, lse, m, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return tuple(download(x) for x in (o, lse, dq, dk, dv))
+
+
+def _check(shape, mask, causal, scale, seed):
+    B, H, N, d = shape
+    inp = synth.qkvdo(seed, shape, "bf16")
+    o, lse, dq, dk, dv = _gpu(inp, mask, causal, scale)
+    bm = mask if mask.ndim == 2 else mask.reshape(B, H, *mask.shape[-2:])
+    o_r, lse_r = BS.forward_blocksparse(inp["q"], inp["k"], inp["v"], bm, causal, scale, BLOCK)
+    g_r = BS.backward_blocksparse(inp["q"], inp["k"], inp["v"], inp["do"], bm, causal, scale, BLOCK)
+    empty = np.isneginf(lse_r)
+    # Rows that may attend nothing: O = 0, LSE = -inf, dQ = 0 exactly.
+    assert np.array_equal(np.isneginf(lse), empty), "empty-row pattern of LSE"
+    assert np.all(o[empty] == 0) and np.all(dq[empty] == 0)
+    live = ~empty
+    assert_close(o[live], o_r[live], "bf16", "O")
+    assert_close(lse[live], lse_r[live], "bf16", "LSE")
+    assert_close(dq, g_r[0], "bf16", "dQ")
+    assert_close(dk, g_r[1], "bf16", "dK")
+    assert_close(dv, g_r[2], "bf16", "dV")
+    return empty.sum()
+
+
+CASES = [
+    # (B, H, N, d, density, per_head)
+    (2, 2, 300, 64, 0.5, False),
+    (1, 3, 300, 128, 0.5, True),
+    (1, 2, 513, 128, 0.35, False),
+    (2, 1, 777, 64, 0.6, True),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", CASES)
+def test_blocksparse_matches_oracle(case, causal):
+    B, H, N, d, density, per_head = case
+    nb = (N + BLOCK - 1) // BLOCK
+    seed = 4000 + N + d + 11 * causal
+    mask = synth.block_mask(seed, nb, density, heads=B * H if per_head else None)
+    _announce("blocksparse", (B, H, N, d), "density", density, "per-head" if per_head else "shared",
+              "causal" if causal else "full", "seed", seed)
+    _check((B, H, N, d), mask, causal, 1.0 / math.sqrt(d), seed)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_empty_query_block_and_empty_key_block(d):
+    # Query block 1 attends nothing (O = 0, LSE = -inf, dQ = 0); key block 2
+    # is attended by nobody (dK = dV = 0 there).
+    B, H, N = 1, 2, 384
+    mask = np.ones((3, 3), np.uint8)
+    mask[1, :] = 0
+    mask[:, 2] = 0
+    _announce("blocksparse empty blocks d", d)
+    n_empty = _check((B, H, N, d), mask, False, 0.125, 4100 + d)
+    assert n_empty == B * H * 128
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_full_mask_equals_dense_bitwise(d, causal):
+    # With every block kept (or, under causal, every block on or below the
+    # diagonal), the block-sparse path does the dense path's arithmetic in the
+    # dense path's order: identical bits.
+    E = _api()
+    B, H, N = 2, 2, 700
+    nb = (N + BLOCK - 1) // BLOCK
+    mask = np.tril(np.ones((nb, nb), np.uint8)) if causal else np.ones((nb, nb), np.uint8)
+    _announce("blocksparse == dense", d, "causal" if causal else "full")
+    inp = synth.qkvdo(4200 + d + causal, (B, H, N, d), "bf16")
+    q, k, v, do = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v", "do"))
+    m = torch.from_numpy(mask).cuda()
+    o1, l1 = E.attn_fwd_blocksparse(q, k, v, m, causal=causal)
+    g1 = E.attn_bwd_blocksparse(q, k, v, o1, do, l1, m, causal=causal)
+    o2, l2 = E.attn_fwd(q, k, v, causal=causal)
+    g2 = E.attn_bwd(q, k, v, o2, do, l2, causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip((o1, l1) + tuple(g1), (o2, l2) + tuple(g2)):
+        assert torch.equal(a, b)
+
+
+def test_mask_layouts_agree():
+    # [nb, nb] shared, [B, H, nb, nb] and [B*H, nb, nb] per head, uint8 and bool.
+    E = _api()
+    B, H, N, d = 2, 2, 300, 64
+    nb = 3
+    shared = synth.block_mask(4300, nb, 0.5)
+    shared[np.arange(nb), np.arange(nb)] = 1
+    inp = synth.qkvdo(4300, (B, H, N, d), "bf16")
+    q, k, v = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v"))
+    outs = []
+    for m in (torch.from_numpy(shared).cuda(),
+              torch.from_numpy(np.ascontiguousarray(np.broadcast_to(shared, (B, H, nb, nb)))).cuda(),
+              torch.from_numpy(np.ascontiguousarray(np.broadcast_to(shared, (B * H, nb, nb)))).cuda(),
+              torch.from_numpy(shared.astype(bool)).cuda()):
+        outs.append(E.attn_fwd_blocksparse(q, k, v, m)[0])
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_sparse_is_faster_than_dense():
+    # 25% of the blocks (diagonal kept): the block-sparse pair of passes takes
+    # clearly less time than the dense pair at N = 4096, d = 128.
+    E = _api()
+    B, H, N, d = 1, 16, 4096, 128
+    nb = N // BLOCK
+    mask = synth.block_mask(4400, nb, 0.25)
+    mask[np.arange(nb), np.arange(nb)] = 1
+    density = mask.mean()
+    _announce("blocksparse speed, density", round(float(density), 3))
+    g = torch.Generator(device="cuda").manual_seed(3)
+    q, k, v, do = (torch.randn(B, H, N, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(4))
+    m = torch.from_numpy(mask).cuda()
+
+    def run(sparse):
+        if sparse:
+            o, l = E.attn_fwd_blocksparse(q, k, v, m)
+            E.attn_bwd_blocksparse(q, k, v, o, do, l, m)
+        else:
+            o, l = E.attn_fwd(q, k, v)
+            E.attn_bwd(q, k, v, o, do, l)
+
+    times = {}
+    for sparse in (False, True):
+        for _ in range(3):
+            run(sparse)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            run(sparse)
+        e1.record()
+        torch.cuda.synchronize()
+        times[sparse] = e0.elapsed_time(e1) / 5
+    print(f"dense {times[False]:.3f} ms, sparse {times[True]:.3f} ms at density {density:.3f}", flush=True)
+    assert times[True] < 0.6 * times[False]
