@@ -8,6 +8,8 @@ dK/dV and dQ.  Inputs are resident in HBM before the timed region starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --sweep           (one JSON line per N, d, mask, pass)
+       python bench.py --blocksparse     (block-sparse vs dense, one JSON line
+                                          per block density and mask)
        python bench.py --profile-pass    (one step plus a plain copy of known
                                           size, for hardware-counter runs)
 
@@ -202,6 +204,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--blocksparse", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -235,6 +238,10 @@ def main():
 
     if args.sweep:
         sweep(torch, E, args.steps, args.warmup)
+        return
+
+    if args.blocksparse:
+        blocksparse(torch, E, args.steps, args.warmup)
         return
 
     shape = (4, 16, 4096, 128)
@@ -340,6 +347,75 @@ def sweep(torch, E, steps, warmup):
                     flush=True,
                 )
             torch.cuda.empty_cache()
+
+
+
+def allowed_pairs(mask, n, block, causal):
+    """Number of (query, key) pairs a block mask (and the causal mask) allows."""
+    idx = np.arange(n) // block
+    total = 0
+    for qb in range(mask.shape[0]):
+        rows = np.arange(qb * block, min(n, (qb + 1) * block))
+        cols = np.nonzero(mask[qb][idx])[0]
+        if causal:
+            total += int(np.sum(cols[None, :] <= rows[:, None]))
+        else:
+            total += len(rows) * len(cols)
+    return total
+
+
+def blocksparse(torch, E, steps, warmup):
+    """Block-sparse forward + backward against dense at B=4 H=16 N=4096 d=128:
+    random 128 x 128 block masks (the diagonal always kept) at several
+    densities.  TFLOP/s counts only the allowed score entries (4 d flops per
+    entry forward, 2.5x that backward)."""
+    import synth
+
+    b, h, n, d = 4, 16, 4096, 128
+    bh = b * h
+    nb = n // E.SPARSE_BLOCK
+    g = torch.Generator(device="cuda").manual_seed(11)
+    q, k, v, do = (torch.randn(b, h, n, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(4))
+    ws = torch.empty(E.attn_bwd_workspace_bytes(b, h, n, d, E.ATTN_BF16), dtype=torch.uint8, device="cuda")
+    for causal in (False, True):
+        dense = None
+        for density in (1.0, 0.5, 0.25):
+            mask = synth.block_mask(5000 + int(100 * density), nb, density)
+            mask[np.arange(nb), np.arange(nb)] = 1
+            m = torch.from_numpy(mask).cuda()
+            pairs = allowed_pairs(mask, n, E.SPARSE_BLOCK, causal) * bh
+
+            def fwd():
+                return E.attn_fwd_blocksparse(q, k, v, m, causal=causal)
+
+            def bwd(o, lse):
+                E.attn_bwd_blocksparse(q, k, v, o, do, lse, m, causal=causal, workspace=ws)
+
+            o, lse = fwd()
+            for _ in range(warmup):
+                fwd()
+                bwd(o, lse)
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+            for s_ in range(steps):
+                ev[3 * s_].record()
+                fwd()
+                ev[3 * s_ + 1].record()
+                bwd(o, lse)
+                ev[3 * s_ + 2].record()
+            torch.cuda.synchronize()
+            fwd_ms = float(np.mean([ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)]))
+            bwd_ms = float(np.mean([ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)]))
+            if density == 1.0:
+                dense = (fwd_ms, bwd_ms)
+            ff = 4.0 * d * pairs
+            print(json.dumps({
+                "blocksparse": True, "B": b, "H": h, "N": n, "d": d, "mask": "causal" if causal else "full",
+                "block": E.SPARSE_BLOCK, "density": round(float(mask.mean()), 4),
+                "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+                "fwd_tflops": round(ff / fwd_ms / 1e9, 1), "bwd_tflops": round(2.5 * ff / bwd_ms / 1e9, 1),
+                "speedup_vs_dense": round((dense[0] + dense[1]) / (fwd_ms + bwd_ms), 3),
+            }), flush=True)
 
 
 if __name__ == "__main__":

@@ -28,6 +28,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int check_mask(const uint8_t* mask, int64_t stride, int64_t B, int64_t H, int64_t N, int dtype) {
   if (!mask) return ATTN_E_NULL;
   if (dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (N > ATTN_SPARSE_MAX_N) return ATTN_E_SHAPE;  // the kernels list a row's tiles in LDS
   const int64_t nb = (N + ATTN_SPARSE_BLOCK - 1) / ATTN_SPARSE_BLOCK;
   if (stride < 0 || (stride != 0 && stride < nb * nb)) return ATTN_E_SHAPE;
   if (stride != 0 && B * H - 1 > (INT64_MAX - nb * nb) / stride) return ATTN_E_SHAPE;

@@ -112,11 +112,14 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   //   [0, 2 KiB)     LSE (x log2 e) and D of up to three query tiles,
   //   Q tiles 0-2, then dO tiles 0-2 (64 rows x D bf16 each),
   //   P exchange     per key group and half tile, lane-major:
-  //                  [group][t][r / 4][lane][r % 4] fp32.
+  //                  [group][t][r / 4][lane][r % 4] fp32,
+  //   (block-sparse only) the list of query tiles to visit and its length.
   // Reads of the dO tiles go through readers shifted by 3 tiles, so that
   // every tile read uses an immediate offset below 64 KiB.
   constexpr int SMALL = 2048, GSHIFT = 3 * TB;
-  __shared__ __attribute__((aligned(1024))) char smem[SMALL + 6 * TB + 4 * 2 * 4 * 64 * 4 * 4];
+  constexpr int PXB = 4 * 2 * 4 * 64 * 4 * 4;  // P exchange bytes
+  constexpr int LISTB = SPARSE ? kMaxSparseTiles * 4 + 16 : 0;  // block-sparse tile list
+  __shared__ __attribute__((aligned(1024))) char smem[SMALL + 6 * TB + PXB + LISTB];
   auto lse_at = [&](auto b) ATTN_INLINE { return reinterpret_cast<float*>(smem + 512 * decltype(b)::value); };
   auto dsm_at = [&](auto b) ATTN_INLINE { return reinterpret_cast<float*>(smem + 512 * decltype(b)::value + 256); };
   auto q_at = [&](auto b) ATTN_INLINE {
@@ -164,22 +167,22 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 
   const int ntq = (n + BQ - 1) / BQ;
   const int it0 = CAUSAL ? (k0 / BQ) : 0;
-  // Block-sparse: a query tile is wanted when its mask block (a 64-row tile
-  // is half of a 128-row block) may attend this key block (a workgroup's 128
-  // keys are one mask block column).  Unwanted tiles are neither fetched nor
-  // computed; the loop still steps through them, so the barriers stay
-  // uniform.
-  const uint8_t* mcol = SPARSE ? bmask + (size_t)bh * mask_stride + kb : nullptr;
-  const int nbq = (n + kSparseBlock - 1) / kSparseBlock;
-  auto want = [&](int i) ATTN_INLINE {
-    if constexpr (SPARSE)
-      return __builtin_amdgcn_readfirstlane(mcol[(size_t)(i >> 1) * nbq]) != 0;
-    else
-      return true;
-  };
   // A tile whose queries all precede this key group is skipped (causal);
   // both waves of a pair decide alike.
-  auto active = [&](int i) ATTN_INLINE { return (!CAUSAL || (i * BQ + BQ - 1 >= kw0)) && want(i); };
+  auto active = [&](int i) ATTN_INLINE { return !CAUSAL || (i * BQ + BQ - 1 >= kw0); };
+
+  // Block-sparse: the query tiles whose mask block (a 64-row tile is half of
+  // a 128-row block) may attend this key block (a workgroup's 128 keys are
+  // one mask block column), listed in LDS in increasing order.
+  uint32_t* const tlist = reinterpret_cast<uint32_t*>(smem + SMALL + 6 * TB + PXB);
+  int* const tcount = reinterpret_cast<int*>(tlist + kMaxSparseTiles);
+  int tcnt = 0;
+  if constexpr (SPARSE) {
+    const uint8_t* mcol = bmask + (size_t)bh * mask_stride + kb;
+    const int nbq = (n + kSparseBlock - 1) / kSparseBlock;
+    tcnt = build_tile_list([&](int i) ATTN_INLINE { return mcol[(size_t)(i >> 1) * nbq] != 0; }, it0, ntq, tlist,
+                           tcount, w, lane);
+  }
 
   // Query rows past n load as zero (Q, dO, LSE, D), so they contribute
   // nothing: P = 1 is finite and multiplies dO = 0 and dS = 0.
@@ -261,27 +264,22 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   // Tile loop skeleton shared by both roles (same barriers in both): tile i
   // lives in buffer b = (i - it0) mod 3.  body(b, i, mid) does the role's
   // work on tile i and calls mid() exactly once, between its two halves.
-  auto run = [&](auto&& body) ATTN_INLINE {
+  auto run_dense = [&](auto&& body) ATTN_INLINE {
     auto step = [&](auto b, int i) ATTN_INLINE {
       constexpr int B = decltype(b)::value;
-      const bool w1 = i + 1 < ntq && want(i + 1);
-      const bool w2 = i + 2 < ntq && want(i + 2);
-      if (w1) load_small(i + 1);
+      if (i + 1 < ntq) load_small(i + 1);
       body(b, i, [&]() ATTN_INLINE {
         __syncthreads();  // P of tile i is published; reads of tile i - 1 are done
-        if (w2) dma(i + 2, int_c<(B + 2) % 3>{});
+        if (i + 2 < ntq) dma(i + 2, int_c<(B + 2) % 3>{});
       });
-      if (w1) store_small(int_c<(B + 1) % 3>{});
-      handover(w2);
+      if (i + 1 < ntq) store_small(int_c<(B + 1) % 3>{});
+      handover(i + 2 < ntq);
     };
-    const bool w0 = want(it0), w1 = it0 + 1 < ntq && want(it0 + 1);
-    if (w0) {
-      load_small(it0);
-      dma(it0, int_c<0>{});
-    }
-    if (w1) dma(it0 + 1, int_c<1>{});
-    if (w0) store_small(int_c<0>{});
-    handover(w1);
+    load_small(it0);
+    dma(it0, int_c<0>{});
+    if (it0 + 1 < ntq) dma(it0 + 1, int_c<1>{});
+    store_small(int_c<0>{});
+    handover(it0 + 1 < ntq);
     for (int it = it0; it < ntq; it += 3) {
       step(int_c<0>{}, it);
       if (it + 1 >= ntq) break;
@@ -289,6 +287,40 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
       if (it + 2 >= ntq) break;
       step(int_c<2>{}, it + 2);
     }
+  };
+  // The same sequence over the listed tiles: position p holds tile T(p) in
+  // buffer p mod 3.
+  auto run_list = [&](auto&& body) ATTN_INLINE {
+    auto T = [&](int p) ATTN_INLINE { return __builtin_amdgcn_readfirstlane((int)tlist[p]); };
+    auto step = [&](auto b, int p) ATTN_INLINE {
+      constexpr int B = decltype(b)::value;
+      if (p + 1 < tcnt) load_small(T(p + 1));
+      body(b, T(p), [&]() ATTN_INLINE {
+        __syncthreads();  // P of this tile is published; reads of the previous one are done
+        if (p + 2 < tcnt) dma(T(p + 2), int_c<(B + 2) % 3>{});
+      });
+      if (p + 1 < tcnt) store_small(int_c<(B + 1) % 3>{});
+      handover(p + 2 < tcnt);
+    };
+    if (tcnt == 0) return;
+    load_small(T(0));
+    dma(T(0), int_c<0>{});
+    if (tcnt > 1) dma(T(1), int_c<1>{});
+    store_small(int_c<0>{});
+    handover(tcnt > 1);
+    for (int p = 0; p < tcnt; p += 3) {
+      step(int_c<0>{}, p);
+      if (p + 1 >= tcnt) break;
+      step(int_c<1>{}, p + 1);
+      if (p + 2 >= tcnt) break;
+      step(int_c<2>{}, p + 2);
+    }
+  };
+  auto run = [&](auto&& body) ATTN_INLINE {
+    if constexpr (SPARSE)
+      run_list(body);
+    else
+      run_dense(body);
   };
 
   if (s_role) {
@@ -403,7 +435,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     });
     // Deferred products of the last tile (no DMA is in flight any more).
     if (pend) {
-      const int bl = (ntq - 1 - it0) % 3;
+      const int bl = (SPARSE ? tcnt - 1 : ntq - 1 - it0) % 3;
       deferred(bl == 0 ? q_at(int_c<0>{}) : bl == 1 ? q_at(int_c<1>{}) : q_at(int_c<2>{}));
     }
   }
@@ -482,15 +514,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   const int kend = CAUSAL ? min(n, q0 + BR) : n;
   const int ntiles = (kend + BC - 1) / BC;
 
-  // Block-sparse: this wave's 32 rows lie in one mask block row.
-  const uint8_t* mrow_w = SPARSE ? bmask + (size_t)bh * mask_stride + (size_t)(wq0 / kSparseBlock) * nb : nullptr;
-
   auto compute = [&](const uint16_t* ks, const uint16_t* vs, int j0) {
     const bool active = !CAUSAL || (j0 <= wq0 + 31);
     if (!active) return;
-    if constexpr (SPARSE) {
-      if (wq0 >= n || __builtin_amdgcn_readfirstlane(mrow_w[j0 / kSparseBlock]) == 0) return;
-    }
     const bool need_mask = (j0 + BC > n) || (CAUSAL && j0 + BC - 1 > wq0);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -549,44 +575,59 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 
   if constexpr (SPARSE) {
     // Key tiles that some query block of this workgroup may attend (BR / 128
-    // mask block rows; a 64-key tile is half of a mask block), in order.
+    // mask block rows; a 64-key tile is half of a mask block), listed in LDS
+    // in increasing order as (tile << 2) | (bit r: block row r wants it).  A
+    // wave computes a listed tile only if its own block row wants it (its 32
+    // rows lie in one block row).
     constexpr int QBLK = BR / kSparseBlock;
-    static_assert(QBLK * kSparseBlock == BR, "workgroups cover whole mask block rows");
+    static_assert(QBLK * kSparseBlock == BR && QBLK <= 2, "workgroups cover one or two mask block rows");
+    __shared__ uint32_t tlist[kMaxSparseTiles];
+    __shared__ int tcount;
     const uint8_t* mrow = bmask + (size_t)bh * mask_stride + (size_t)(q0 / kSparseBlock) * nb;
     const int nrows = min(QBLK, nb - q0 / kSparseBlock);
-    auto wanted = [&](int j) ATTN_INLINE {
-      bool any = false;
-      for (int r = 0; r < nrows; ++r)
-        any = any || __builtin_amdgcn_readfirstlane(mrow[(size_t)r * nb + (j >> 1)]) != 0;
-      return any;
+    const int qsub = (wq0 - q0) / kSparseBlock;
+    // Tile indices here are below 2^11 (the list's capacity), so the row
+    // bits fit below them.
+    const int cnt = build_tile_list(
+        [&](int j) ATTN_INLINE {
+          bool any = false;
+          for (int r = 0; r < nrows; ++r) any = any || mrow[(size_t)r * nb + (j >> 1)] != 0;
+          return any;
+        },
+        0, ntiles, tlist, &tcount, w, lane);
+    if (w == 0) {
+      for (int p = lane; p < cnt; p += 64) {
+        const uint32_t j = tlist[p];
+        uint32_t bits = 0;
+        for (int r = 0; r < nrows; ++r) bits |= (mrow[(size_t)r * nb + (j >> 1)] != 0 ? 1u : 0u) << r;
+        tlist[p] = (j << 2) | bits;
+      }
+    }
+    __syncthreads();
+    auto tile = [&](int p) ATTN_INLINE { return __builtin_amdgcn_readfirstlane((int)tlist[p]); };
+    auto run_tile = [&](const uint16_t* ks, const uint16_t* vs, int e) ATTN_INLINE {
+      if ((e >> qsub) & 1) compute(ks, vs, (e >> 2) * BC);
     };
-    auto next = [&](int j) ATTN_INLINE {
-      while (j < ntiles && !wanted(j)) ++j;
-      return j;
-    };
-    int jc = next(0);
-    if (jc < ntiles) {
-      dma_tile<D, NW>(rk, k0s, jc * BC, w, lane);
-      dma_tile<D, NW>(rv, v0s, jc * BC, w, lane);
+    if (cnt > 0) {
+      dma_tile<D, NW>(rk, k0s, (tile(0) >> 2) * BC, w, lane);
+      dma_tile<D, NW>(rv, v0s, (tile(0) >> 2) * BC, w, lane);
       wait_vmem();
       __syncthreads();
     }
-    while (jc < ntiles) {
-      const int jn = next(jc + 1);
-      if (jn < ntiles) {
-        dma_tile<D, NW>(rk, k1s, jn * BC, w, lane);
-        dma_tile<D, NW>(rv, v1s, jn * BC, w, lane);
+    for (int p = 0; p < cnt; p += 2) {
+      if (p + 1 < cnt) {
+        dma_tile<D, NW>(rk, k1s, (tile(p + 1) >> 2) * BC, w, lane);
+        dma_tile<D, NW>(rv, v1s, (tile(p + 1) >> 2) * BC, w, lane);
       }
-      compute(k0s, v0s, jc * BC);
+      run_tile(k0s, v0s, tile(p));
       wait_vmem();
       __syncthreads();
-      if (jn >= ntiles) break;
-      jc = next(jn + 1);
-      if (jc < ntiles) {
-        dma_tile<D, NW>(rk, k0s, jc * BC, w, lane);
-        dma_tile<D, NW>(rv, v0s, jc * BC, w, lane);
+      if (p + 1 >= cnt) break;
+      if (p + 2 < cnt) {
+        dma_tile<D, NW>(rk, k0s, (tile(p + 2) >> 2) * BC, w, lane);
+        dma_tile<D, NW>(rv, v0s, (tile(p + 2) >> 2) * BC, w, lane);
       }
-      compute(k1s, v1s, jn * BC);
+      run_tile(k1s, v1s, tile(p + 1));
       wait_vmem();
       __syncthreads();
     }

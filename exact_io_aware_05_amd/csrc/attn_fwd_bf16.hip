@@ -175,36 +175,35 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   if constexpr (SPARSE) {
     // Block-sparse: only the key tiles of the blocks this query block may
     // attend are fetched and computed (a workgroup's 128 rows are exactly one
-    // mask block row; a 64-key tile is half of a mask block).
+    // mask block row; a 64-key tile is half of a mask block).  Their indices
+    // are listed in LDS first, then walked like the dense sequence.
     static_assert(BR == kSparseBlock, "one workgroup per mask block row");
+    __shared__ uint32_t tlist[kMaxSparseTiles];
+    __shared__ int tcount;
     const uint8_t* mrow = bmask + (size_t)bh * mask_stride + (size_t)qb * nb;
-    auto next = [&](int j) ATTN_INLINE {
-      while (j < ntiles && __builtin_amdgcn_readfirstlane(mrow[j >> 1]) == 0) ++j;
-      return j;
-    };
-    int jc = next(0);
-    if (jc < ntiles) {
-      dma_tile<D, NW>(rk, k0s, jc * BC, w, lane);
-      dma_tile<D, NW>(rv, v0s, jc * BC, w, lane);
+    const int cnt = build_tile_list([&](int j) ATTN_INLINE { return mrow[j >> 1] != 0; }, 0, ntiles, tlist, &tcount,
+                                    w, lane);
+    auto tile = [&](int p) ATTN_INLINE { return __builtin_amdgcn_readfirstlane((int)tlist[p]); };
+    if (cnt > 0) {
+      dma_tile<D, NW>(rk, k0s, tile(0) * BC, w, lane);
+      dma_tile<D, NW>(rv, v0s, tile(0) * BC, w, lane);
       wait_vmem();
       __syncthreads();
     }
-    while (jc < ntiles) {
-      const int jn = next(jc + 1);
-      if (jn < ntiles) {
-        dma_tile<D, NW>(rk, k1s, jn * BC, w, lane);
-        dma_tile<D, NW>(rv, v1s, jn * BC, w, lane);
+    for (int p = 0; p < cnt; p += 2) {
+      if (p + 1 < cnt) {
+        dma_tile<D, NW>(rk, k1s, tile(p + 1) * BC, w, lane);
+        dma_tile<D, NW>(rv, v1s, tile(p + 1) * BC, w, lane);
       }
-      compute(k0s, v0s, jc * BC);
+      compute(k0s, v0s, tile(p) * BC);
       wait_vmem();
       __syncthreads();
-      if (jn >= ntiles) break;
-      jc = next(jn + 1);
-      if (jc < ntiles) {
-        dma_tile<D, NW>(rk, k0s, jc * BC, w, lane);
-        dma_tile<D, NW>(rv, v0s, jc * BC, w, lane);
+      if (p + 1 >= cnt) break;
+      if (p + 2 < cnt) {
+        dma_tile<D, NW>(rk, k0s, tile(p + 2) * BC, w, lane);
+        dma_tile<D, NW>(rv, v0s, tile(p + 2) * BC, w, lane);
       }
-      compute(k1s, v1s, jn * BC);
+      compute(k1s, v1s, tile(p + 1) * BC);
       wait_vmem();
       __syncthreads();
     }

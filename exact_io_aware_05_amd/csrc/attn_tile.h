@@ -151,4 +151,29 @@ struct TileReader {
   }
 };
 
+// Block-sparse tile list.  Wave 0 of the workgroup writes, in increasing
+// order, the tile indices j in [j0, j1) with want(j) true into `list` (LDS,
+// at most kMaxSparseTiles entries) and the count into *count; every thread
+// returns the count after the barrier.  want(j) is evaluated by one lane per
+// tile (64 tiles per round: ballot, then each wanted lane writes its slot).
+constexpr int kMaxSparseTiles = 2048;
+
+template <typename F>
+__device__ __forceinline__ int build_tile_list(F want, int j0, int j1, uint32_t* list, int* count, int w, int lane) {
+  if (w == 0) {
+    int cnt = 0;
+    for (int c = j0; c < j1; c += 64) {
+      const int j = c + lane;
+      const bool f = j < j1 && want(j);
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(f);
+      const int pre = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      if (f) list[cnt + pre] = (uint32_t)j;
+      cnt += __builtin_popcountll(bal);
+    }
+    if (lane == 0) *count = cnt;
+  }
+  __syncthreads();
+  return __builtin_amdgcn_readfirstlane(*count);
+}
+
 }  // namespace attn

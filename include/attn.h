@@ -168,10 +168,12 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
  * Other arguments, layouts, ownership and errors as for attn_fwd / attn_bwd;
  * attn_bwd_blocksparse must get the mask and causal flag given to
  * attn_fwd_blocksparse, and the same workspace size as attn_bwd.  bf16 only
- * (ATTN_FP32 returns ATTN_E_UNSUPPORTED); a NULL mask is ATTN_E_NULL, a
- * stride out of range ATTN_E_SHAPE.  Deterministic, like the dense calls.
+ * (ATTN_FP32 returns ATTN_E_UNSUPPORTED); N at most ATTN_SPARSE_MAX_N; a NULL
+ * mask is ATTN_E_NULL, a stride out of range or a larger N ATTN_E_SHAPE.
+ * Deterministic, like the dense calls.
  */
 #define ATTN_SPARSE_BLOCK 128
+#define ATTN_SPARSE_MAX_N 131072
 
 int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o,
                          float* lse, int64_t B, int64_t H, int64_t N,

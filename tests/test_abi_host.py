@@ -145,6 +145,7 @@ def test_blocksparse_argument_validation():
     assert fwd(mask=None) == -1 and bwd(mask=None) == -1
     assert fwd(dtype=1) == -3 and bwd(dtype=1) == -3  # bf16 only
     assert fwd(d=96) == -3 and fwd(N=0) == -2
+    assert fwd(N=131073) == -2 and bwd(N=131073) == -2  # beyond ATTN_SPARSE_MAX_N
     assert fwd(stride=-1) == -2 and bwd(stride=nb * nb - 1) == -2
     assert fwd(stride=2**62) == -2  # last head's mask not addressable
     assert fwd(scale=float("nan")) == -4

@@ -65,6 +65,7 @@ CASES = [
     (1, 3, 300, 128, 0.5, True),
     (1, 2, 513, 128, 0.35, False),
     (2, 1, 777, 64, 0.6, True),
+    (1, 2, 4200, 64, 0.3, True),  # 66 key tiles: the tile lists take two rounds
 ]
 
 
