@@ -688,7 +688,9 @@ hipError_t launch_dkdv(const BwdArgs& a) {
 
 template <int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_dq(const BwdArgs& a) {
-  constexpr int NW = D == 128 ? ATTN_DQ_NW128 : 4;
+  // Block-sparse: one mask block row per workgroup (4 waves), so that every
+  // wave of a workgroup wants every tile the workgroup fetches.
+  constexpr int NW = (D == 128 && !SPARSE) ? ATTN_DQ_NW128 : 4;
   const int n = (int)a.n;
   const int nqb = (n + NW * 32 - 1) / (NW * 32);
   const int total = (int)(a.bh * nqb);
