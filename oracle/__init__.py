@@ -28,6 +28,9 @@ Modules:
 * :mod:`oracle.blocksparse` -- the same definition under a block mask (the
   block-sparse variant named in "Experiments & Results" on the Paper Notes
   page), with the conventions for rows that allow no key.
+* :mod:`oracle.varlen` -- unequal query and key lengths (bottom-right causal
+  alignment) and the split-K/V merge by the two-block rule of "Tiling:
+  Block-by-Block Softmax".
 
 Every function here is pinned by ``tests/test_oracle*.py`` against page-printed
 values, closed forms, invariants, finite differences and a library autograd;
