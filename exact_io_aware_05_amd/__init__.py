@@ -13,6 +13,8 @@ Entry points carry the C names:
   three phases of the backward pass, for use on separate streams or timing
 * :func:`attn_fwd_blocksparse`, :func:`attn_bwd_blocksparse` -- the same
   with a block mask over 128 x 128 blocks of the score matrix
+* :func:`attn_fwd_qk`, :func:`attn_bwd_qk` -- queries and keys of different
+  lengths (bottom-right causal alignment), with split-K/V for the forward
 * :func:`attn_bwd_workspace_bytes`, :func:`attn_status_string`
 * :func:`lib` -- the raw ``ctypes.CDLL``.
 """
@@ -30,6 +32,8 @@ __all__ = [
     "attn_fwd_blocksparse",
     "attn_bwd_blocksparse",
     "SPARSE_BLOCK",
+    "attn_fwd_qk",
+    "attn_bwd_qk",
     "attn_bwd_workspace_bytes",
     "attn_status_string",
     "lib",
@@ -86,6 +90,16 @@ def lib():
     L.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp,
                                        i64, vp, ctypes.c_size_t, vp]
     L.attn_bwd_blocksparse.restype = i32
+    L.attn_fwd_qk_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32, i32]
+    L.attn_fwd_qk_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_fwd_qk.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, f32, i32, vp, ctypes.c_size_t,
+                              vp]
+    L.attn_fwd_qk.restype = i32
+    L.attn_bwd_qk_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+    L.attn_bwd_qk_workspace_bytes.restype = ctypes.c_size_t
+    L.attn_bwd_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, f32, vp,
+                              ctypes.c_size_t, vp]
+    L.attn_bwd_qk.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -320,4 +334,70 @@ def attn_bwd_blocksparse(q, k, v, o, do, lse, block_mask, causal=False, scale=No
     )
     if st != 0:
         raise AttnError(st, "attn_bwd_blocksparse")
+    return dq, dk, dv
+
+
+def _qk_shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    _check([("q", q)], (B, H, Nq, d), q.dtype, q.device)
+    _check([("k", k), ("v", v)], (B, H, Nk, d), q.dtype, q.device)
+    return B, H, Nq, Nk, d
+
+
+def attn_fwd_qk(q, k, v, causal=False, scale=None, num_splits=1, out=None, lse=None, workspace=None):
+    """Forward with Nq queries and Nk keys (bottom-right causal alignment:
+    query i sees key j when j <= i + Nk - Nq).  ``num_splits``: 1 = one pass,
+    2..64 = split-K/V into at most that many key chunks merged afterwards,
+    0 = chosen from the shape.  bf16 only.  Returns (o, lse)."""
+    torch = _torch()
+    B, H, Nq, Nk, d = _qk_shapes(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    need = int(lib().attn_fwd_qk_workspace_bytes(B, H, Nq, Nk, d, code, int(num_splits)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check([("out", out)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, Nq), torch.float32, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib().attn_fwd_qk(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d, code,
+        int(bool(causal)), float(scale), int(num_splits), ws_ptr, ws_bytes, _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_fwd_qk")
+    return out, lse
+
+
+def attn_bwd_qk(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, grads=None):
+    """Backward for Nq queries and Nk keys (same causal and scale as the
+    forward); returns (dq, dk, dv)."""
+    torch = _torch()
+    B, H, Nq, Nk, d = _qk_shapes(q, k, v)
+    _check([("o", o), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, Nq), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    need = int(lib().attn_bwd_qk_workspace_bytes(B, H, Nq, Nk, d, code))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    _check([("dq", dq)], q.shape, q.dtype, q.device)
+    _check([("dk", dk), ("dv", dv)], k.shape, q.dtype, q.device)
+    st = lib().attn_bwd_qk(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), B, H, Nq, Nk, d, code, int(bool(causal)), float(scale),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_bwd_qk")
     return dq, dk, dv

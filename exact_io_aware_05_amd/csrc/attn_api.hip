@@ -58,6 +58,40 @@ attn::BwdArgs make_bwd(const void* q, const void* k, const void* v, const void* 
   return a;
 }
 
+// Split-K/V plan for attn_fwd_qk: number of chunks and keys per chunk.
+struct SplitPlan {
+  int nsplit;
+  int kchunk;
+};
+
+SplitPlan split_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int num_splits) {
+  const int64_t ktiles = (Nk + 63) / 64;
+  int64_t want = num_splits;
+  if (num_splits == 0) {
+    // Enough workgroups to fill the chip twice over (256 CUs, two per CU),
+    // each chunk at least 4 tiles.
+    const int64_t wgs = B * H * ((Nq + 127) / 128);
+    want = (1024 + wgs - 1) / wgs;
+    want = want < ktiles / 4 ? want : ktiles / 4;
+  }
+  if (want > 64) want = 64;
+  if (want > ktiles) want = ktiles;
+  if (want < 2) return SplitPlan{1, (int)(ktiles * 64)};
+  const int64_t tiles_per = (ktiles + want - 1) / want;
+  const int64_t ns = (ktiles + tiles_per - 1) / tiles_per;
+  if (ns < 2) return SplitPlan{1, (int)(ktiles * 64)};
+  return SplitPlan{(int)ns, (int)(tiles_per * 64)};
+}
+
+int check_qk(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype) {
+  int st = check_shape(B, H, Nq, d, dtype);
+  if (st != ATTN_OK) return st;
+  st = check_shape(B, H, Nk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -200,6 +234,76 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
       make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
   a.bmask = block_mask;
   a.mask_stride = mask_head_stride;
+  if (attn::bwd_dsum(a, true) != hipSuccess) return ATTN_E_HIP;
+  if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
+  if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
+}
+
+size_t attn_fwd_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype,
+                                   int num_splits) {
+  if (check_qk(B, H, Nq, Nk, d, dtype) != ATTN_OK || num_splits < 0 || num_splits > 64) return 0;
+  const SplitPlan sp = split_plan(B, H, Nq, Nk, num_splits);
+  if (sp.nsplit < 2) return 0;
+  const size_t rows = (size_t)(B * H * Nq) * (size_t)sp.nsplit;
+  return align256(rows * (size_t)d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+int attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Nq,
+                int64_t Nk, int64_t d, int dtype, int causal, float scale, int num_splits, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  const int st = check_qk(B, H, Nq, Nk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (num_splits < 0 || num_splits > 64) return ATTN_E_SHAPE;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  const SplitPlan sp = split_plan(B, H, Nq, Nk, num_splits);
+  const size_t need = attn_fwd_qk_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits);
+  if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
+    return ATTN_E_WORKSPACE;
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = B * H;
+  a.n = Nq;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  a.nk = Nk;
+  a.nsplit = sp.nsplit;
+  a.kchunk = sp.kchunk;
+  if (sp.nsplit > 1) {
+    const size_t rows = (size_t)(B * H * Nq) * (size_t)sp.nsplit;
+    a.opart = (float*)workspace;
+    a.lpart = (float*)((char*)workspace + align256(rows * (size_t)d * sizeof(float)));
+  }
+  if (attn::fwd_bf16(a) != hipSuccess) return ATTN_E_HIP;
+  if (sp.nsplit > 1 && attn::fwd_combine(a) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
+}
+
+size_t attn_bwd_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype) {
+  if (check_qk(B, H, Nq, Nk, d, dtype) != ATTN_OK) return 0;
+  return align256((size_t)(B * H * Nq) * sizeof(float));
+}
+
+int attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype,
+                int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  const int st = check_qk(B, H, Nq, Nk, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  if (!workspace || workspace_bytes < attn_bwd_qk_workspace_bytes(B, H, Nq, Nk, d, dtype) ||
+      ((uintptr_t)workspace & 255) != 0)
+    return ATTN_E_WORKSPACE;
+  attn::BwdArgs a =
+      make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, Nq, d, causal, scale, stream);
+  a.nk = Nk;
   if (attn::bwd_dsum(a, true) != hipSuccess) return ATTN_E_HIP;
   if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
   if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;

@@ -94,7 +94,7 @@ __device__ __forceinline__ void pipeline_reads2() {
 template <int N>
 using int_c = std::integral_constant<int, N>;
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool QK>
 __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ K,
                                                         const uint16_t* __restrict__ V,
@@ -103,7 +103,8 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
                                                         const float* __restrict__ Dsum,
                                                         uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                                                         int n, int nkb, int total, float scale, float sl2e,
-                                                        const uint8_t* __restrict__ bmask, long long mask_stride) {
+                                                        const uint8_t* __restrict__ bmask, long long mask_stride,
+                                                        int nk_arg, int coff_arg) {
   constexpr int NW = 8, BKV = 128, BQ = 64;
   constexpr int TB = BQ * D * 2;  // bytes per 64-row tile
   constexpr int IPW = (D / 8) / NW;  // DMA loads per wave per tile
@@ -143,8 +144,13 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   const int k0 = kb * BKV;
   const int kw0 = k0 + 32 * grp;
   const int key = kw0 + l32;
+  // Unequal lengths (QK): n is the query length, nk the key length, and
+  // query i sees key j when j <= i + coff (causal, bottom-right).
+  const int nk = QK ? nk_arg : n;
+  const int coff = (QK && CAUSAL) ? coff_arg : 0;
 
   const size_t head = (size_t)bh * (size_t)n * D;
+  const size_t khead = (size_t)bh * (size_t)nk * D;
   const uint32_t head_bytes = (uint32_t)n * D * 2u;
   const auto rq = make_rsrc(Q + head, head_bytes);
   const auto rdo = make_rsrc(dO + head, head_bytes);
@@ -154,7 +160,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   // B operands of S (K rows) for the S wave, of dP (V rows) for the dP wave.
   bf16x8 bf[D / 16];
   {
-    const auto rkv = make_rsrc((s_role ? K : V) + head, head_bytes);
+    const auto rkv = make_rsrc((s_role ? K : V) + khead, (uint32_t)nk * D * 2u);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) bf[s] = as_bf16x8(bload16(rkv, (uint32_t)key * (D * 2) + 32 * s + 16 * hh));
   }
@@ -166,10 +172,10 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     for (int r = 0; r < 16; ++r) acc[e][r] = 0.f;
 
   const int ntq = (n + BQ - 1) / BQ;
-  const int it0 = CAUSAL ? (k0 / BQ) : 0;
+  const int it0 = CAUSAL ? max(0, k0 - coff) / BQ : 0;
   // A tile whose queries all precede this key group is skipped (causal);
   // both waves of a pair decide alike.
-  auto active = [&](int i) ATTN_INLINE { return !CAUSAL || (i * BQ + BQ - 1 >= kw0); };
+  auto active = [&](int i) ATTN_INLINE { return !CAUSAL || (i * BQ + BQ - 1 >= kw0 - coff); };
 
   // Block-sparse: the query tiles whose mask block (a 64-row tile is half of
   // a 128-row block) may attend this key block (a workgroup's 128 keys are
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
           c1[r] = 0.f;
         }
         chains(TR, q_at(b), c0, c1);
-        const bool need_mask = CAUSAL && (i * BQ < kw0 + 31);
+        const bool need_mask = CAUSAL && (i * BQ < kw0 + 31 - coff);
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -351,7 +357,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
               float pv = fast_exp2(fmaf(t == 0 ? c0[4 * g + k] : c1[4 * g + k], sl2e, -l4[k]));
               if (need_mask) {
                 const int q = i * BQ + 32 * t + 8 * g + 4 * hh + k;
-                pv = key > q ? 0.f : pv;
+                pv = key > q + coff ? 0.f : pv;
               }
               v[t][4 * g + k] = pv;
               o[k] = pv;
@@ -440,8 +446,8 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     }
   }
 
-  if (key < n) {
-    uint16_t* row = (s_role ? dV : dK) + head + (size_t)key * D;
+  if (key < nk) {
+    uint16_t* row = (s_role ? dV : dK) + khead + (size_t)key * D;
     const float f = s_role ? 1.0f : scale;
 #pragma unroll
     for (int e = 0; e < D / 32; ++e)
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // dQ: query-stationary
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool CAUSAL, bool SPARSE>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __restrict__ Q,
                                                            const uint16_t* __restrict__ K,
                                                            const uint16_t* __restrict__ V,
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
                                                            uint16_t* __restrict__ dQ, int n, int nqb, int total,
                                                            float scale, float sl2e,
                                                            const uint8_t* __restrict__ bmask, long long mask_stride,
-                                                           int nb) {
+                                                           int nb, int nk_arg, int coff_arg) {
   constexpr int BR = NW * 32, BC = 64;
 
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[BC * D];
@@ -489,12 +495,17 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   const int wq0 = q0 + 32 * w;
   const int qrow = wq0 + l32;
 
+  // Unequal lengths (QK): n is the query length, nk the key length, and
+  // query i sees key j when j <= i + coff (causal, bottom-right).
+  const int nk = QK ? nk_arg : n;
+  const int coff = (QK && CAUSAL) ? coff_arg : 0;
   const size_t head = (size_t)bh * (size_t)n * D;
+  const size_t khead = (size_t)bh * (size_t)nk * D;
   const uint32_t head_bytes = (uint32_t)n * D * 2u;
   const auto rq = make_rsrc(Q + head, head_bytes);
   const auto rdo = make_rsrc(dO + head, head_bytes);
-  const auto rk = make_rsrc(K + head, head_bytes);
-  const auto rv = make_rsrc(V + head, head_bytes);
+  const auto rk = make_rsrc(K + khead, (uint32_t)nk * D * 2u);
+  const auto rv = make_rsrc(V + khead, (uint32_t)nk * D * 2u);
 
   bf16x8 qf[D / 16], gf[D / 16];
 #pragma unroll
@@ -511,13 +522,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 #pragma unroll
     for (int r = 0; r < 16; ++r) dqa[e][r] = 0.f;
 
-  const int kend = CAUSAL ? min(n, q0 + BR) : n;
-  const int ntiles = (kend + BC - 1) / BC;
+  const int kend = CAUSAL ? min(nk, q0 + BR + coff) : nk;
+  const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
 
   auto compute = [&](const uint16_t* ks, const uint16_t* vs, int j0) {
-    const bool active = !CAUSAL || (j0 <= wq0 + 31);
+    const bool active = !CAUSAL || (j0 <= wq0 + 31 + coff);
     if (!active) return;
-    const bool need_mask = (j0 + BC > n) || (CAUSAL && j0 + BC - 1 > wq0);
+    const bool need_mask = (j0 + BC > nk) || (CAUSAL && j0 + BC - 1 > wq0 + coff);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       // One half tile at a time: interleaving the halves costs more
@@ -547,7 +558,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kj = j0 + 32 * t + crow(r, hh);
-            x[r] = kj > qrow ? -INFINITY : x[r];
+            x[r] = kj > qrow + coff ? -INFINITY : x[r];
           }
         }
 #pragma unroll
@@ -559,7 +570,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pv = fast_exp2(fmaf(sacc[r], sl2e, -l2));
-          if (need_mask) pv = (j0 + 32 * t + crow(r, hh) >= n) ? 0.f : pv;
+          if (need_mask) pv = (j0 + 32 * t + crow(r, hh) >= nk) ? 0.f : pv;
           ds[r] = pv * (pacc[r] - dq_d);
         }
       }
@@ -632,10 +643,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
       __syncthreads();
     }
   } else {
-  dma_tile<D, NW>(rk, k0s, 0, w, lane);
-  dma_tile<D, NW>(rv, v0s, 0, w, lane);
-  wait_vmem();
-  __syncthreads();
+  if (!QK || ntiles > 0) {
+    dma_tile<D, NW>(rk, k0s, 0, w, lane);
+    dma_tile<D, NW>(rv, v0s, 0, w, lane);
+    wait_vmem();
+    __syncthreads();
+  }
 
   for (int jt = 0; jt < ntiles; jt += 2) {
     if (jt + 1 < ntiles) {
@@ -670,15 +683,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool QK>
 hipError_t launch_dkdv(const BwdArgs& a) {
   const int n = (int)a.n;
-  const int nkb = (n + 127) / 128;
+  const int nk = QK ? (int)a.nk : n;
+  const int nkb = (nk + 127) / 128;
   const int total = (int)(a.bh * nkb);
-  hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, SPARSE>), dim3(total), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, SPARSE, QK>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e,
-                     a.bmask, (long long)a.mask_stride);
+                     a.bmask, (long long)a.mask_stride, nk, nk - n);
   return hipGetLastError();
 }
 
@@ -686,7 +700,7 @@ hipError_t launch_dkdv(const BwdArgs& a) {
 #define ATTN_DQ_NW128 8  // waves per dQ workgroup at d = 128 (tuning knob)
 #endif
 
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool QK>
 hipError_t launch_dq(const BwdArgs& a) {
   // Block-sparse: one mask block row per workgroup (4 waves), so that every
   // wave of a workgroup wants every tile the workgroup fetches.
@@ -695,29 +709,38 @@ hipError_t launch_dq(const BwdArgs& a) {
   const int nqb = (n + NW * 32 - 1) / (NW * 32);
   const int total = (int)(a.bh * nqb);
   const int nb = (n + kSparseBlock - 1) / kSparseBlock;
-  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE>), dim3(total), dim3(NW * 64), 0, a.stream,
+  const int nk = QK ? (int)a.nk : n;
+  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK>), dim3(total), dim3(NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.dsum, (uint16_t*)a.dq, n, nqb, total, a.scale, a.scale * kLog2e, a.bmask,
-                     (long long)a.mask_stride, nb);
+                     (long long)a.mask_stride, nb, nk, nk - n);
   return hipGetLastError();
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool QK>
 hipError_t dkdv_t(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_dkdv<64, true, SPARSE>(a) : launch_dkdv<64, false, SPARSE>(a);
-  return a.causal ? launch_dkdv<128, true, SPARSE>(a) : launch_dkdv<128, false, SPARSE>(a);
+  if (a.d == 64) return a.causal ? launch_dkdv<64, true, SPARSE, QK>(a) : launch_dkdv<64, false, SPARSE, QK>(a);
+  return a.causal ? launch_dkdv<128, true, SPARSE, QK>(a) : launch_dkdv<128, false, SPARSE, QK>(a);
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool QK>
 hipError_t dq_t(const BwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_dq<64, true, SPARSE>(a) : launch_dq<64, false, SPARSE>(a);
-  return a.causal ? launch_dq<128, true, SPARSE>(a) : launch_dq<128, false, SPARSE>(a);
+  if (a.d == 64) return a.causal ? launch_dq<64, true, SPARSE, QK>(a) : launch_dq<64, false, SPARSE, QK>(a);
+  return a.causal ? launch_dq<128, true, SPARSE, QK>(a) : launch_dq<128, false, SPARSE, QK>(a);
 }
 
 }  // namespace
 
-hipError_t bwd_bf16_dkdv(const BwdArgs& a) { return a.bmask ? dkdv_t<true>(a) : dkdv_t<false>(a); }
+hipError_t bwd_bf16_dkdv(const BwdArgs& a) {
+  if (a.bmask) return dkdv_t<true, false>(a);
+  if (a.nk >= 0) return dkdv_t<false, true>(a);
+  return dkdv_t<false, false>(a);
+}
 
-hipError_t bwd_bf16_dq(const BwdArgs& a) { return a.bmask ? dq_t<true>(a) : dq_t<false>(a); }
+hipError_t bwd_bf16_dq(const BwdArgs& a) {
+  if (a.bmask) return dq_t<true, false>(a);
+  if (a.nk >= 0) return dq_t<false, true>(a);
+  return dq_t<false, false>(a);
+}
 
 }  // namespace attn

@@ -39,7 +39,7 @@
 
 namespace attn {
 
-template <int D, int NW, bool CAUSAL, bool SPARSE>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
                                                               const uint16_t* __restrict__ K,
                                                               const uint16_t* __restrict__ V,
@@ -47,7 +47,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
                                                               float* __restrict__ LSE, int n, int nqb,
                                                               int total, float c, uint32_t qsign,
                                                               const uint8_t* __restrict__ bmask,
-                                                              long long mask_stride, int nb) {
+                                                              long long mask_stride, int nb, QkKernelArgs qa) {
   constexpr int BC = 64;                // keys per tile
   constexpr int BR = NW * 32;           // query rows per workgroup
   constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
@@ -64,16 +64,26 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   const TileReader<D> TR(lane);
 
   // Logical tile: contiguous per XCD; heavy (late) query blocks first.
+  // Unequal lengths (QK): n is the query length, nk the key length; with
+  // split-K/V a workgroup owns one query block and one chunk of keys.
+  const int nsplit = QK ? qa.nsplit : 1;
   const int lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / nqb;
-  const int qb = CAUSAL ? (nqb - 1 - lid % nqb) : (lid % nqb);
+  const int per_head = nqb * nsplit;
+  const int bh = lid / per_head;
+  const int rem = lid % per_head;
+  const int qi = QK ? rem / nsplit : rem;
+  const int sp = QK ? rem % nsplit : 0;
+  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
   const int q0 = qb * BR;
+  const int nk = QK ? qa.nk : n;
 
   const size_t head = (size_t)bh * (size_t)n * D;
+  const size_t khead = (size_t)bh * (size_t)nk * D;
   const uint32_t head_bytes = (uint32_t)n * D * 2u;
+  const uint32_t khead_bytes = (uint32_t)nk * D * 2u;
   const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rk = make_rsrc(K + head, head_bytes);
-  const auto rv = make_rsrc(V + head, head_bytes);
+  const auto rk = make_rsrc(K + khead, khead_bytes);
+  const auto rv = make_rsrc(V + khead, khead_bytes);
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds its query's 8
   // consecutive features per 16-feature step.  Rows past n read as zero.
@@ -86,9 +96,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
     qf[s] = as_bf16x8(u);
   }
 
-  // Key range visited by this workgroup.
-  const int kend = CAUSAL ? min(n, q0 + BR) : n;
-  const int ntiles = (kend + BC - 1) / BC;
+  // Keys of this workgroup: [klo, khi) (its split; all keys when square),
+  // keys >= khi masked; causal (bottom-right when lengths differ: query i
+  // sees key j when j <= i + coff) visits only up to kend.  Tiles jlo ..
+  // ntiles - 1.
+  const int coff = (QK && CAUSAL) ? qa.coff : 0;
+  const int klo = QK ? sp * qa.kchunk : 0;
+  const int khi = QK ? min(nk, klo + qa.kchunk) : n;
+  const int kend = CAUSAL ? min(khi, q0 + BR + coff) : khi;
+  const int jlo = klo / BC;
+  const int ntiles = kend > klo ? (kend + BC - 1) / BC : jlo;
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -101,7 +118,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   const int wq0 = q0 + 32 * w;  // first query of this wave
 
   auto compute = [&](const uint16_t* kb, const uint16_t* vb, int j0) {
-    const bool active = !CAUSAL || (j0 <= wq0 + 31);
+    const bool active = !CAUSAL || (j0 <= wq0 + 31 + coff);
     if (!active) return;
     f32x16 sacc[2];
 #pragma unroll
@@ -115,14 +132,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
     }
 
     // Mask (diagonal and ragged tiles only) and take this query's tile max.
-    const bool need_mask = (j0 + BC > n) || (CAUSAL && j0 + BC - 1 > wq0);
+    const bool need_mask = (j0 + BC > khi) || (CAUSAL && j0 + BC - 1 > wq0 + coff);
     if (need_mask) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + 32 * t + crow(r, hh);
-          const bool dead = (key >= n) || (CAUSAL && key > qrow);
+          const bool dead = (key >= khi) || (CAUSAL && key > qrow + coff);
           sacc[t][r] = dead ? -INFINITY : sacc[t][r];
         }
     }
@@ -134,11 +151,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
     mx = half_max(mx);
 
     // Raise the reference max only when some row outgrew it by > 2^tau.
-    // Tile 0 always holds key 0, which every query may see, so the
-    // reference is finite from the first tile on.
+    // Square: tile 0 always holds key 0, which every query may see, so the
+    // reference is finite from the first tile on.  Unequal lengths: a row
+    // may see no key of its first tiles, so its reference can stay -inf;
+    // then nothing is rescaled and its probabilities are 0.
     if (__builtin_amdgcn_ballot_w64(mx > mref + tau_raw) != 0) {
       const float m_new = fmaxf(mref, mx);
-      const float alpha = fast_exp2((mref - m_new) * c);
+      const float alpha = (QK && m_new == -INFINITY) ? 1.f : fast_exp2((mref - m_new) * c);
       mref = m_new;
       lsum *= alpha;
 #pragma unroll
@@ -146,7 +165,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha;
     }
-    const float mc = mref * c;
+    const float mc = (QK && mref == -INFINITY) ? 0.f : mref * c;
 
     bf16x8 pf[2][2];
 #pragma unroll
@@ -208,12 +227,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
       __syncthreads();
     }
   } else {
-  dma_tile<D, NW>(rk, k0s, 0, w, lane);
-  dma_tile<D, NW>(rv, v0s, 0, w, lane);
-  wait_vmem();
-  __syncthreads();
+  if (!QK || jlo < ntiles) {
+    dma_tile<D, NW>(rk, k0s, jlo * BC, w, lane);
+    dma_tile<D, NW>(rv, v0s, jlo * BC, w, lane);
+    wait_vmem();
+    __syncthreads();
+  }
 
-  for (int jt = 0; jt < ntiles; jt += 2) {
+  for (int jt = jlo; jt < ntiles; jt += 2) {
     // Even tile from buffer 0; tile jt+1 streams into buffer 1.
     if (jt + 1 < ntiles) {
       dma_tile<D, NW>(rk, k1s, (jt + 1) * BC, w, lane);
@@ -235,10 +256,30 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   }
 
   // Epilogue: O = acc / l (bf16, nearest-even), LSE = (m c + log2 l) ln 2.
-  // Block-sparse rows that may attend no key have l = 0: O = 0 and
-  // LSE = -inf (m stayed -inf).
+  // Rows that may attend no key (block-sparse, unequal lengths, or a split
+  // with none of the row's keys) have l = 0: O = 0 and LSE = -inf.
   const float ltot = half_sum(lsum);
-  const float inv = (SPARSE && ltot == 0.f) ? 0.f : 1.0f / ltot;
+  const bool empty = (SPARSE || QK) && ltot == 0.f;
+  const float inv = empty ? 0.f : 1.0f / ltot;
+  const float lse_v = empty ? -INFINITY : (mref * c + fast_log2(ltot)) * kLn2;
+  if (QK && nsplit > 1) {
+    // Split-K/V: this chunk's normalised output and LSE, in fp32.
+    if (qrow < n) {
+      const size_t prow = ((size_t)bh * nsplit + sp) * (size_t)n + qrow;
+      float* orow = qa.opart + prow * D;
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 o4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = oacc[e][4 * g + i] * inv;
+          *reinterpret_cast<f32x4*>(orow + 32 * e + 8 * g + 4 * hh) = o4;
+        }
+      if (hh == 0) qa.lpart[prow] = lse_v;
+    }
+    return;
+  }
   if (qrow < n) {
     uint16_t* orow = O + head + (size_t)qrow * D;
 #pragma unroll
@@ -250,15 +291,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
         o2[1] = pack_bf16x2(oacc[e][4 * g + 2] * inv, oacc[e][4 * g + 3] * inv);
         *reinterpret_cast<u32x2*>(orow + 32 * e + 8 * g + 4 * hh) = o2;
       }
-    if (hh == 0) LSE[(size_t)bh * n + qrow] = (mref * c + fast_log2(ltot)) * kLn2;
+    if (hh == 0) LSE[(size_t)bh * n + qrow] = lse_v;
   }
 }
 
-template <int D, int NW, bool CAUSAL, bool SPARSE>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK>
 static hipError_t launch_fwd(const FwdArgs& a) {
   constexpr int BR = NW * 32;
   const int nqb = (int)((a.n + BR - 1) / BR);
-  const int total = (int)(a.bh * nqb);
+  const int nsplit = QK ? a.nsplit : 1;
+  const int total = (int)(a.bh * nqb * nsplit);
   // |scale| below ~7e-31 (including 0) is raised to a normal float: the
   // exponent arguments then differ from the exact ones by < 1e-28 and the
   // lazy-rescale threshold tau / c stays finite.
@@ -266,18 +308,93 @@ static hipError_t launch_fwd(const FwdArgs& a) {
   if (c < 1e-30f) c = 1e-30f;
   const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;
   const int nb = (int)((a.n + kSparseBlock - 1) / kSparseBlock);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE>), dim3(total), dim3(NW * 64), 0, a.stream,
+  QkKernelArgs qa{};
+  if (QK) {
+    qa.nk = (int)a.nk;
+    qa.coff = (int)(a.nk - a.n);
+    qa.kchunk = nsplit > 1 ? a.kchunk : (int)((a.nk + 63) / 64 * 64);
+    qa.nsplit = nsplit;
+    qa.opart = a.opart;
+    qa.lpart = a.lpart;
+  }
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK>), dim3(total), dim3(NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb);
+                     (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb, qa);
   return hipGetLastError();
 }
 
-template <bool SPARSE>
+template <bool SPARSE, bool QK>
 static hipError_t fwd_bf16_t(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_fwd<64, 4, true, SPARSE>(a) : launch_fwd<64, 4, false, SPARSE>(a);
-  return a.causal ? launch_fwd<128, 4, true, SPARSE>(a) : launch_fwd<128, 4, false, SPARSE>(a);
+  if (a.d == 64)
+    return a.causal ? launch_fwd<64, 4, true, SPARSE, QK>(a) : launch_fwd<64, 4, false, SPARSE, QK>(a);
+  return a.causal ? launch_fwd<128, 4, true, SPARSE, QK>(a) : launch_fwd<128, 4, false, SPARSE, QK>(a);
 }
 
-hipError_t fwd_bf16(const FwdArgs& a) { return a.bmask ? fwd_bf16_t<true>(a) : fwd_bf16_t<false>(a); }
+hipError_t fwd_bf16(const FwdArgs& a) {
+  if (a.bmask) return fwd_bf16_t<true, false>(a);
+  if (a.nk >= 0) return fwd_bf16_t<false, true>(a);
+  return fwd_bf16_t<false, false>(a);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K/V merge: one wave per query row.  With the chunks' LSE values l_s
+// and normalised outputs o_s, LSE = log sum_s exp(l_s) and
+// O = sum_s exp(l_s - LSE) o_s -- the two-block rule of "Tiling:
+// Block-by-Block Softmax" (Paper Notes) applied to all chunks at once, in
+// the (LSE, normalised O) form.  A row that no chunk saw gets O = 0 and
+// LSE = -inf.  At most 64 chunks.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ opart,
+                                                      const float* __restrict__ lpart, uint16_t* __restrict__ O,
+                                                      float* __restrict__ LSE, int n, int nsplit, long long rows) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // row = bh * n + i
+  if (row >= rows) return;
+  const long long bh = row / n, i = row % n;
+  const float ls = lane < nsplit ? lpart[(bh * nsplit + lane) * n + i] : -INFINITY;
+  float mx = ls;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  constexpr int F = D / 64;  // features per lane
+  float acc[F];
+#pragma unroll
+  for (int f = 0; f < F; ++f) acc[f] = 0.f;
+  float lse = -INFINITY;
+  if (mx != -INFINITY) {
+    const float wl = lane < nsplit ? expf(ls - mx) : 0.f;
+    float sum = wl;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+    lse = mx + logf(sum);
+    for (int s = 0; s < nsplit; ++s) {
+      const float ws = __shfl(wl, s) / sum;
+      if (ws != 0.f) {
+        const float* src = opart + ((bh * nsplit + s) * n + i) * D;
+#pragma unroll
+        for (int f = 0; f < F; ++f) acc[f] += ws * src[lane + 64 * f];
+      }
+    }
+  }
+  uint16_t* dst = O + row * D;
+#pragma unroll
+  for (int f = 0; f < F; ++f) {
+    const uint32_t two = pack_bf16x2(acc[f], 0.f);
+    dst[lane + 64 * f] = (uint16_t)(two & 0xFFFFu);
+  }
+  if (lane == 0) LSE[row] = lse;
+}
+
+hipError_t fwd_combine(const FwdArgs& a) {
+  const long long rows = (long long)(a.bh * a.n);
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (a.d == 64)
+    hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, a.stream, a.opart, a.lpart, (uint16_t*)a.o, a.lse,
+                       (int)a.n, a.nsplit, rows);
+  else
+    hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(256), 0, a.stream, a.opart, a.lpart, (uint16_t*)a.o,
+                       a.lse, (int)a.n, a.nsplit, rows);
+  return hipGetLastError();
+}
 
 }  // namespace attn

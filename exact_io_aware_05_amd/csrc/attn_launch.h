@@ -25,6 +25,26 @@ struct FwdArgs {
   // (0: one mask for every head).  nullptr: dense.
   const uint8_t* bmask = nullptr;
   int64_t mask_stride = 0;
+  // Unequal lengths (bf16 only): `n` is then the query length and nk the key
+  // length (nk < 0: square); causal alignment is bottom-right.  With
+  // nsplit > 1 the keys are cut into chunks of kchunk (a multiple of 64) and
+  // each chunk's normalised output (fp32 [bh, nsplit, n, d]) and LSE
+  // ([bh, nsplit, n]) go to opart / lpart, to be merged by fwd_combine.
+  int64_t nk = -1;
+  int nsplit = 1;
+  int kchunk = 0;
+  float* opart = nullptr;
+  float* lpart = nullptr;
+};
+
+// Kernel-side view of the unequal-length arguments.
+struct QkKernelArgs {
+  int nk;      // key length
+  int coff;    // causal offset nk - n: query i sees key j when j <= i + coff
+  int kchunk;  // keys per split
+  int nsplit;
+  float* opart;
+  float* lpart;
 };
 
 struct BwdArgs {
@@ -46,12 +66,15 @@ struct BwdArgs {
   hipStream_t stream;
   const uint8_t* bmask = nullptr;  // as in FwdArgs
   int64_t mask_stride = 0;
+  int64_t nk = -1;  // as in FwdArgs (no split in the backward)
 };
 
 // Block size of the block-sparse mask (query and key rows per block).
 constexpr int kSparseBlock = 128;
 
 hipError_t fwd_bf16(const FwdArgs& a);
+// Merge of the split-K/V partial results into O (bf16) and LSE.
+hipError_t fwd_combine(const FwdArgs& a);
 hipError_t fwd_f32(const FwdArgs& a);
 // Backward phases; `o` is read only by bwd_dsum, `dq` written only by the
 // *_dq launchers, `dk`/`dv` only by the *_dkdv launchers.

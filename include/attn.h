@@ -189,6 +189,50 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v,
                          int64_t mask_head_stride, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * Queries and keys of different lengths: q, o, dout, dq are [B, H, Nq, d],
+ * k, v, dk, dv are [B, H, Nk, d], lse and the backward workspace's D are
+ * [B, H, Nq].  The pages fix no causal alignment for unequal lengths; here it
+ * is bottom-right, the alignment of Nq queries that follow Nk - Nq earlier
+ * tokens (decoding, chunked prefill): query i sees key j when
+ * j <= i + (Nk - Nq).  With Nq > Nk the first Nq - Nk rows see no key and get
+ * O = 0, LSE = -inf, dQ = 0.  Nq == Nk is the square case of attn_fwd.
+ *
+ * Split-K/V (for few queries over many keys): the keys are cut into
+ * num_splits chunks of whole 64-key tiles, each chunk's (normalised O, LSE)
+ * per row goes to the workspace, and a second kernel merges them by the
+ * two-block rule of "Tiling: Block-by-Block Softmax" (Paper Notes), in the
+ * form LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+ * num_splits = 1: no split (no workspace); 2..64: at most that many chunks
+ * (fewer if Nk has fewer tiles); 0: chosen by the library from the shape.
+ *
+ *   attn_fwd_qk_workspace_bytes : bytes attn_fwd_qk needs for this shape and
+ *                                 num_splits (0 when no split is used, or on
+ *                                 an invalid argument)
+ *   attn_bwd_qk_workspace_bytes : bytes attn_bwd_qk needs (D, [B, H, Nq])
+ *
+ * Other arguments, ownership and errors as for attn_fwd / attn_bwd.  bf16 only
+ * (ATTN_FP32 returns ATTN_E_UNSUPPORTED); num_splits outside 0..64 is
+ * ATTN_E_SHAPE; a workspace that is NULL (when needed), too small or not
+ * 256-byte aligned is ATTN_E_WORKSPACE.  Deterministic.
+ */
+size_t attn_fwd_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                   int64_t d, int dtype, int num_splits);
+
+int attn_fwd_qk(const void* q, const void* k, const void* v, void* o,
+                float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                int64_t d, int dtype, int causal, float scale, int num_splits,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+size_t attn_bwd_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                   int64_t d, int dtype);
+
+int attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
+                const void* dout, const float* lse, void* dq, void* dk,
+                void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                int64_t d, int dtype, int causal, float scale, void* workspace,
+                size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);
 

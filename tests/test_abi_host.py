@@ -32,9 +32,13 @@ def test_header_declares_the_boundary():
         "attn_bwd_dkdv",
         "attn_bwd_dq",
         "attn_bwd_dsum",
+        "attn_bwd_qk",
+        "attn_bwd_qk_workspace_bytes",
         "attn_bwd_workspace_bytes",
         "attn_fwd",
         "attn_fwd_blocksparse",
+        "attn_fwd_qk",
+        "attn_fwd_qk_workspace_bytes",
         "attn_status_string",
     ]
 
@@ -151,6 +155,44 @@ def test_blocksparse_argument_validation():
     assert fwd(scale=float("nan")) == -4
     assert bwd(ws=None) == -5 and bwd(ws=FAKE * 256 + 8) == -5
     assert E.SPARSE_BLOCK == 128
+
+
+def test_unequal_lengths_validation_and_workspace():
+    E, L = _lib()
+
+    def fwd(ptrs=(FAKE,) * 5, Nq=5, Nk=300, dtype=0, splits=1, ws=None, wsb=0, scale=0.1):
+        return L.attn_fwd_qk(*ptrs, 2, 3, Nq, Nk, 64, dtype, 1, scale, splits, ws, wsb, None)
+
+    def bwd(ptrs=(FAKE,) * 9, Nq=5, Nk=300, dtype=0, ws=FAKE * 256, wsb=None):
+        if wsb is None:
+            wsb = L.attn_bwd_qk_workspace_bytes(2, 3, Nq, Nk, 64, 0)
+        return L.attn_bwd_qk(*ptrs, 2, 3, Nq, Nk, 64, dtype, 1, 0.1, ws, wsb, None)
+
+    for i in range(5):
+        ptrs = [FAKE] * 5
+        ptrs[i] = None
+        assert fwd(ptrs=ptrs) == -1
+    for i in range(9):
+        ptrs = [FAKE] * 9
+        ptrs[i] = None
+        assert bwd(ptrs=ptrs) == -1
+    assert fwd(dtype=1) == -3 and bwd(dtype=1) == -3
+    assert fwd(Nq=0) == -2 and fwd(Nk=0) == -2 and bwd(Nk=2**31) == -2
+    assert fwd(splits=-1) == -2 and fwd(splits=65) == -2
+    assert fwd(scale=float("nan")) == -4
+    # A split needs a workspace: sized by the query, refused when absent or short.
+    need = L.attn_fwd_qk_workspace_bytes(2, 3, 5, 300, 64, 0, 4)
+    rows = 2 * 3 * 5 * 4  # 300 keys = 5 tiles; at most 4 chunks of 2 tiles -> 3 chunks
+    assert need > 0 and need % 256 == 0
+    assert need == L.attn_fwd_qk_workspace_bytes(2, 3, 5, 300, 64, 0, 3)
+    assert need <= ((rows * 64 * 4 + 255) // 256 + (rows * 4 + 255) // 256) * 256
+    assert fwd(splits=4) == -5 and fwd(splits=4, ws=FAKE * 256, wsb=need - 1) == -5
+    assert fwd(splits=4, ws=FAKE * 256 + 16, wsb=need) == -5
+    assert L.attn_fwd_qk_workspace_bytes(2, 3, 5, 300, 64, 0, 1) == 0
+    assert L.attn_fwd_qk_workspace_bytes(2, 3, 5, 64, 64, 0, 8) == 0  # one key tile: nothing to split
+    assert L.attn_fwd_qk_workspace_bytes(2, 3, 5, 300, 64, 1, 4) == 0  # fp32: invalid
+    assert bwd(ws=None) == -5 and bwd(wsb=L.attn_bwd_qk_workspace_bytes(2, 3, 5, 300, 64, 0) - 1) == -5
+    assert L.attn_bwd_qk_workspace_bytes(2, 3, 5, 300, 64, 0) == ((2 * 3 * 5 * 4 + 255) // 256) * 256
 
 
 def test_workspace_size():

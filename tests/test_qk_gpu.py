@@ -1,0 +1,122 @@
+"""GPU parity of attention with unequal query and key lengths (bottom-right
+causal alignment) and of the split-K/V forward, through the C ABI, against
+the float64 oracle of oracle/varlen.py."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import varlen as VL
+from tests.gpu_util import assert_close, download, upload
+
+pytestmark = [pytest.mark.gpu]
+
+
+def _api():
+    import exact_io_aware_05_amd as E
+
+    E.lib()
+    return E
+
+
+def _announce(*a):
+    print("[case]", *a, flush=True)
+
+
+def _inputs(seed, B, H, nq, nk, d):
+    qi = synth.qkvdo(seed, (B, H, nq, d), "bf16")
+    ki = synth.qkvdo(seed + 1, (B, H, nk, d), "bf16", with_do=False)
+    return {"q": qi["q"], "q_raw": qi["q_raw"], "do": qi["do"], "do_raw": qi["do_raw"],
+            "k": ki["k"], "k_raw": ki["k_raw"], "v": ki["v"], "v_raw": ki["v_raw"]}
+
+
+def _check_fwd(o, lse, o_r, lse_r):
+    empty = np.isneginf(lse_r)
+    assert np.array_equal(np.isneginf(lse), empty), "empty-row pattern of LSE"
+    assert np.all(o[empty] == 0)
+    live = ~empty
+    assert_close(o[live], o_r[live], "bf16", "O")
+    assert_close(lse[live], lse_r[live], "bf16", "LSE")
+
+
+CASES = [
+    # (B, H, Nq, Nk, d): queries after a cache, ragged; more queries than keys
+    (2, 2, 200, 700, 64),
+    (1, 3, 77, 1000, 128),
+    (2, 2, 300, 130, 64),
+    (1, 2, 129, 64, 128),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", CASES)
+def test_unequal_lengths_forward_and_backward(case, causal):
+    E = _api()
+    B, H, nq, nk, d = case
+    seed = 6000 + nq + nk + d + causal
+    _announce("qk fwd+bwd", case, "causal" if causal else "full", "seed", seed)
+    inp = _inputs(seed, B, H, nq, nk, d)
+    q, k, v, do = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = E.attn_fwd_qk(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = E.attn_bwd_qk(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], causal, scale)
+    g_r = VL.backward_qk_batched(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale)
+    _check_fwd(download(o), download(lse), o_r, lse_r)
+    empty = np.isneginf(lse_r)
+    assert np.all(download(dq)[empty] == 0)
+    assert_close(download(dq), g_r[0], "bf16", "dQ")
+    assert_close(download(dk), g_r[1], "bf16", "dK")
+    assert_close(download(dv), g_r[2], "bf16", "dV")
+
+
+@pytest.mark.parametrize("splits", [1, 3, 8, 0])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,d", [(1, 128), (16, 64)])
+def test_decode_split_kv(nq, d, causal, splits):
+    E = _api()
+    B, H, nk = 2, 4, 5000
+    seed = 6100 + nq + d + causal
+    _announce("decode", (B, H, nq, nk, d), "causal" if causal else "full", "splits", splits)
+    inp = _inputs(seed, B, H, nq, nk, d)
+    q, k, v = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v"))
+    o, lse = E.attn_fwd_qk(q, k, v, causal=causal, num_splits=splits)
+    torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], causal)
+    _check_fwd(download(o), download(lse), o_r, lse_r)
+
+
+def test_long_decode_auto_split():
+    # Four queries after 65532 cached tokens, one head group, automatic split.
+    E = _api()
+    B, H, nq, nk, d = 1, 4, 4, 65536, 128
+    _announce("decode long", (B, H, nq, nk, d))
+    inp = _inputs(6200, B, H, nq, nk, d)
+    q, k, v = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v"))
+    assert E.lib().attn_fwd_qk_workspace_bytes(B, H, nq, nk, d, E.ATTN_BF16, 0) > 0
+    o, lse = E.attn_fwd_qk(q, k, v, causal=True, num_splits=0)
+    torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], True)
+    _check_fwd(download(o), download(lse), o_r, lse_r)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_equal_lengths_match_square_path_bitwise(d, causal):
+    # Nq == Nk without a split does the square path's arithmetic in its order.
+    E = _api()
+    B, H, n = 2, 2, 333
+    _announce("qk == square", d, "causal" if causal else "full")
+    inp = synth.qkvdo(6300 + d + causal, (B, H, n, d), "bf16")
+    q, k, v, do = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v", "do"))
+    o1, l1 = E.attn_fwd_qk(q, k, v, causal=causal)
+    g1 = E.attn_bwd_qk(q, k, v, o1, do, l1, causal=causal)
+    o2, l2 = E.attn_fwd(q, k, v, causal=causal)
+    g2 = E.attn_bwd(q, k, v, o2, do, l2, causal=causal)
+    torch.cuda.synchronize()
+    for a, b in zip((o1, l1) + tuple(g1), (o2, l2) + tuple(g2)):
+        assert torch.equal(a, b)
