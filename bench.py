@@ -10,6 +10,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        python bench.py --sweep           (one JSON line per N, d, mask, pass)
        python bench.py --blocksparse     (block-sparse vs dense, one JSON line
                                           per block density and mask)
+       python bench.py --decode          (unequal lengths: split-K/V decoding
+                                          and chunked prefill, one JSON line each)
        python bench.py --profile-pass    (one step plus a plain copy of known
                                           size, for hardware-counter runs)
 
@@ -205,6 +207,7 @@ def main():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--blocksparse", action="store_true")
+    ap.add_argument("--decode", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -242,6 +245,10 @@ def main():
 
     if args.blocksparse:
         blocksparse(torch, E, args.steps, args.warmup)
+        return
+
+    if args.decode:
+        decode(torch, E, args.steps, args.warmup)
         return
 
     shape = (4, 16, 4096, 128)
@@ -416,6 +423,61 @@ def blocksparse(torch, E, steps, warmup):
                 "fwd_tflops": round(ff / fwd_ms / 1e9, 1), "bwd_tflops": round(2.5 * ff / bwd_ms / 1e9, 1),
                 "speedup_vs_dense": round((dense[0] + dense[1]) / (fwd_ms + bwd_ms), 3),
             }), flush=True)
+
+
+
+def _time_ms(torch, fn, steps, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def decode(torch, E, steps, warmup):
+    """Unequal lengths.  Decoding: one query per head after Nk cached tokens
+    (B=1, H=32, d=128, causal bottom-right), HBM-bound: reported as the K and V
+    bytes read per second against 8 TB/s, with one pass and with the
+    library's split-K/V choice.  Chunked prefill: 1024 queries after 7168
+    cached tokens (B=1, H=16, d=128, causal): TFLOP/s over the allowed pairs,
+    forward (library's split choice) and backward."""
+    g = torch.Generator(device="cuda").manual_seed(13)
+    b, h, d = 1, 32, 128
+    for nk in (4096, 16384, 65536):
+        q = torch.randn(b, h, 1, d, device="cuda", generator=g).to(torch.bfloat16)
+        k, v = (torch.randn(b, h, nk, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
+        kv_bytes = 2.0 * b * h * nk * d * 2
+        for splits in (1, 0):
+            nsplit_bytes = E.lib().attn_fwd_qk_workspace_bytes(b, h, 1, nk, d, E.ATTN_BF16, splits)
+            ws = torch.empty(max(nsplit_bytes, 256), dtype=torch.uint8, device="cuda")
+            ms = _time_ms(torch, lambda: E.attn_fwd_qk(q, k, v, causal=True, num_splits=splits, workspace=ws),
+                          steps, warmup)
+            gbs = kv_bytes / (ms * 1e-3) / 1e9
+            print(json.dumps({
+                "decode": True, "B": b, "H": h, "Nq": 1, "Nk": nk, "d": d, "causal": True,
+                "num_splits": "auto" if splits == 0 else splits, "ms": round(ms, 4),
+                "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            }), flush=True)
+    b, h, nq, nk = 1, 16, 1024, 8192
+    q, do = (torch.randn(b, h, nq, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
+    k, v = (torch.randn(b, h, nk, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
+    pairs = b * h * sum(min(nk, i + (nk - nq) + 1) for i in range(nq))
+    o, lse = E.attn_fwd_qk(q, k, v, causal=True, num_splits=0)
+    fwd_ms = _time_ms(torch, lambda: E.attn_fwd_qk(q, k, v, causal=True, num_splits=0), steps, warmup)
+    bwd_ms = _time_ms(torch, lambda: E.attn_bwd_qk(q, k, v, o, do, lse, causal=True), steps, warmup)
+    ff = 4.0 * d * pairs
+    print(json.dumps({
+        "chunked_prefill": True, "B": b, "H": h, "Nq": nq, "Nk": nk, "d": d, "causal": True,
+        "fwd_ms": round(fwd_ms, 4), "bwd_ms": round(bwd_ms, 4),
+        "fwd_tflops": round(ff / fwd_ms / 1e9, 1), "bwd_tflops": round(2.5 * ff / bwd_ms / 1e9, 1),
+        "fwd_frac_peak": round(ff / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+        "bwd_frac_peak": round(2.5 * ff / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+    }), flush=True)
 
 
 if __name__ == "__main__":

@@ -337,26 +337,31 @@ hipError_t fwd_bf16(const FwdArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split-K/V merge: one wave per query row.  With the chunks' LSE values l_s
-// and normalised outputs o_s, LSE = log sum_s exp(l_s) and
-// O = sum_s exp(l_s - LSE) o_s -- the two-block rule of "Tiling:
+// Split-K/V merge: WPR waves per query row, 4 waves per workgroup.  With the
+// chunks' LSE values l_s and normalised outputs o_s, LSE = log sum_s
+// exp(l_s) and O = sum_s exp(l_s - LSE) o_s -- the two-block rule of "Tiling:
 // Block-by-Block Softmax" (Paper Notes) applied to all chunks at once, in
-// the (LSE, normalised O) form.  A row that no chunk saw gets O = 0 and
-// LSE = -inf.  At most 64 chunks.
+// the (LSE, normalised O) form.  With WPR = 4 (few rows, as in decoding) wave
+// w sums chunks w, w + 4, ... and the partial sums meet in LDS; with WPR = 1
+// (many rows) each wave sums one row's chunks.  A row that no chunk saw gets
+// O = 0 and LSE = -inf.  At most 64 chunks.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int WPR>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ opart,
                                                       const float* __restrict__ lpart, uint16_t* __restrict__ O,
                                                       float* __restrict__ LSE, int n, int nsplit, long long rows) {
+  constexpr int F = D / 64;  // features per lane
+  __shared__ float red[WPR > 1 ? WPR - 1 : 1][D];
   const int lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // row = bh * n + i
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = wave % WPR;  // this wave's share of the row's chunks
+  const long long row = (long long)blockIdx.x * (4 / WPR) + wave / WPR;  // bh * n + i
   if (row >= rows) return;
   const long long bh = row / n, i = row % n;
   const float ls = lane < nsplit ? lpart[(bh * nsplit + lane) * n + i] : -INFINITY;
   float mx = ls;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  constexpr int F = D / 64;  // features per lane
   float acc[F];
 #pragma unroll
   for (int f = 0; f < F; ++f) acc[f] = 0.f;
@@ -367,33 +372,50 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
     lse = mx + logf(sum);
-    for (int s = 0; s < nsplit; ++s) {
-      const float ws = __shfl(wl, s) / sum;
-      if (ws != 0.f) {
-        const float* src = opart + ((bh * nsplit + s) * n + i) * D;
+    const float inv = 1.0f / sum;
+    // Every chunk wrote finite partials (zeros where it saw nothing), so the
+    // loads are unconditional and independent.
+#pragma unroll 4
+    for (int s = w; s < nsplit; s += WPR) {
+      const float ws = __shfl(wl, s) * inv;
+      const float* src = opart + ((bh * nsplit + s) * n + i) * D;
 #pragma unroll
-        for (int f = 0; f < F; ++f) acc[f] += ws * src[lane + 64 * f];
-      }
+      for (int f = 0; f < F; ++f) acc[f] += ws * src[lane + 64 * f];
     }
+  }
+  if constexpr (WPR > 1) {
+    if (w > 0) {
+#pragma unroll
+      for (int f = 0; f < F; ++f) red[w - 1][lane + 64 * f] = acc[f];
+    }
+    __syncthreads();
+    if (w != 0) return;
+#pragma unroll
+    for (int f = 0; f < F; ++f)
+#pragma unroll
+      for (int r = 0; r < WPR - 1; ++r) acc[f] += red[r][lane + 64 * f];
   }
   uint16_t* dst = O + row * D;
 #pragma unroll
-  for (int f = 0; f < F; ++f) {
-    const uint32_t two = pack_bf16x2(acc[f], 0.f);
-    dst[lane + 64 * f] = (uint16_t)(two & 0xFFFFu);
-  }
+  for (int f = 0; f < F; ++f) dst[lane + 64 * f] = (uint16_t)(pack_bf16x2(acc[f], 0.f) & 0xFFFFu);
   if (lane == 0) LSE[row] = lse;
 }
 
+template <int D, int WPR>
+static void launch_combine(const FwdArgs& a, long long rows) {
+  const dim3 grid((unsigned)((rows + (4 / WPR) - 1) / (4 / WPR)));
+  hipLaunchKernelGGL((combine_kernel<D, WPR>), grid, dim3(256), 0, a.stream, a.opart, a.lpart, (uint16_t*)a.o,
+                     a.lse, (int)a.n, a.nsplit, rows);
+}
+
 hipError_t fwd_combine(const FwdArgs& a) {
+  // Below about four rows per CU, spread each row over a workgroup.
   const long long rows = (long long)(a.bh * a.n);
-  const dim3 grid((unsigned)((rows + 3) / 4));
+  const bool few = rows < 1024;
   if (a.d == 64)
-    hipLaunchKernelGGL((combine_kernel<64>), grid, dim3(256), 0, a.stream, a.opart, a.lpart, (uint16_t*)a.o, a.lse,
-                       (int)a.n, a.nsplit, rows);
+    few ? launch_combine<64, 4>(a, rows) : launch_combine<64, 1>(a, rows);
   else
-    hipLaunchKernelGGL((combine_kernel<128>), grid, dim3(256), 0, a.stream, a.opart, a.lpart, (uint16_t*)a.o,
-                       a.lse, (int)a.n, a.nsplit, rows);
+    few ? launch_combine<128, 4>(a, rows) : launch_combine<128, 1>(a, rows);
   return hipGetLastError();
 }
 
