@@ -1,38 +1,44 @@
 // Fused exact attention forward, bf16 in / bf16 out, fp32 accumulation, gfx950.
 //
 // One workgroup owns a block of BR = 32 * NW query rows of one (batch, head)
-// and streams the head's keys and values past it in tiles of BC = 64 rows,
-// keeping the running row max m, running sum l and the unnormalised output in
-// registers ("Tiling: Block-by-Block Softmax" on the Paper Notes page; the
-// loop of "build it from scratch" on the "flash attention" page and of
-// "Rescale and accumulate" on the aicassindra page).  The N x N score matrix
-// exists only one 64 x 32 tile at a time, per wave, in registers.
+// and streams the head's keys and values past it, keeping the running row
+// max m, running sum l and the unnormalised output in registers ("Tiling:
+// Block-by-Block Softmax" on the Paper Notes page; the loop of "build it from
+// scratch" on the "flash attention" page and of "Rescale and accumulate" on
+// the aicassindra page).  The N x N score matrix exists only one 32 x 32
+// block at a time, per wave, in registers.
 //
 // Layout choices (MI355X-specific):
-//  * Each wave owns 32 query rows.  It computes the transposed score tile
-//    S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so lane l holds all scores of
-//    one query (l % 32) for 16 keys per 32-key sub-tile; the row max and row
-//    sum are in-lane, plus one v_permlane32_swap between the wave halves.
+//  * Each wave owns 32 query rows.  It computes transposed score blocks
+//    S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so lane l holds the scores of
+//    one query (l % 32) for 16 of the block's 32 keys; the row sums are
+//    in-lane, plus one v_permlane32_swap between the wave halves at the end.
 //  * The transposed output O^T = V^T P^T takes P^T straight from the score
 //    registers as the B operand (no LDS round trip for P).  The V^T operand
 //    comes from the row-major V tile through transposing LDS reads.
-//  * K and V tiles are fetched by buffer->LDS DMA into two buffers: the DMA
-//    of tile j+1 is in flight while tile j is computed (no staging
-//    registers, no staging instructions); one barrier per tile.  Rows past
-//    the end of the head arrive as zeros, so ragged tails need no branches.
+//  * Software pipeline over units of 32 keys: step u issues the score
+//    products of unit u + 1 and the output products of unit u - 1, and
+//    between them the exponentials of unit u, so every wave always has
+//    vector work to overlap with its own matrix products.
+//  * K and V tiles (64 keys) are fetched by buffer->LDS DMA into two rings of
+//    R tiles (no staging registers); V is consumed one tile after K, so the
+//    fetch of tile t + R - 1 (K) and t + R - 2 (V) is issued at the barrier
+//    that opens tile t.  Rows past the end of the head arrive as zeros.
 //  * Softmax in base 2: the exponent argument is one FMA, x * c - m * c with
 //    c = |scale| log2(e); a negative scale is folded into Q by flipping the
 //    sign bits of its bf16 values (exact).  The row sum adds the fp32
 //    probabilities, so LSE (which the backward pass recomputes P from) keeps
 //    fp32 accuracy.
-//  * Lazy rescaling: the reference max used for exp2 is raised only when some
-//    row's max grows by more than 2^8 over it (a wave-uniform decision), so
-//    the output accumulator is rarely rescaled.  l and O always share the
-//    same reference, so the result is the same exact softmax; probabilities
-//    stay below 2^8 before normalisation.
+//  * Lazy rescaling without a per-block max: the probabilities of a unit are
+//    computed against the current reference max m, and only if some lane's
+//    sum over the unit exceeds 2^8 (so possibly one probability does) is the
+//    unit's max taken, m raised, the output and sum rescaled and the unit
+//    recomputed.  l and O always share m, so the result is the same exact
+//    softmax; probabilities stay at most 2^8 before normalisation, and a row
+//    whose m is still -inf (nothing seen yet) always takes that path.
 //  * Causal: key tiles beyond the workgroup's last query are never visited;
-//    a wave skips tiles that lie wholly above its own rows; masking code runs
-//    only on diagonal and ragged-tail tiles.
+//    units wholly above a wave's rows are skipped by that wave; masking code
+//    runs only on diagonal and ragged-tail units, which come last.
 #include "attn_device.h"
 #include "attn_launch.h"
 #include "attn_tile.h"
@@ -40,28 +46,44 @@
 namespace attn {
 
 template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
-                                                              const uint16_t* __restrict__ K,
-                                                              const uint16_t* __restrict__ V,
-                                                              uint16_t* __restrict__ O,
-                                                              float* __restrict__ LSE, int n, int nqb,
-                                                              int total, float c, uint32_t qsign,
-                                                              const uint8_t* __restrict__ bmask,
-                                                              long long mask_stride, int nb, QkKernelArgs qa) {
-  constexpr int BC = 64;                // keys per tile
-  constexpr int BR = NW * 32;           // query rows per workgroup
-  constexpr float kTau = 8.0f;          // lazy-rescale threshold, log2 units
-
-  __shared__ __attribute__((aligned(1024))) uint16_t k0s[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v0s[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t k1s[BC * D];
-  __shared__ __attribute__((aligned(1024))) uint16_t v1s[BC * D];
-
+__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
+                                                                   const uint16_t* __restrict__ K,
+                                                                   const uint16_t* __restrict__ V,
+                                                                   uint16_t* __restrict__ O,
+                                                                   float* __restrict__ LSE, int n, int nqb,
+                                                                   int total, float c, uint32_t qsign,
+                                                                   const uint8_t* __restrict__ bmask,
+                                                                   long long mask_stride, int nb, QkKernelArgs qa) {
+  constexpr int BC = 64;               // keys per K/V tile
+  constexpr int BU = 32;               // keys per pipeline unit (half a tile)
+  constexpr int BR = NW * 32;          // query rows per workgroup
+  constexpr int R = NW == 8 ? 3 : 2;   // tiles per ring
+  constexpr int TB = BC * D;           // elements per tile
+  constexpr int IPW = (D / 8) / NW;    // DMA loads per wave per tile
+  constexpr float kGate = 256.0f;      // 2^8
+  // Ring slots are separate LDS arrays, always addressed at compile-time
+  // slots: the compiler can then tell a DMA into one slot from reads of
+  // another, and waits for the DMA only where its slot is read.
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[TB], k1s[TB], k2s[R > 2 ? TB : 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TB], v1s[TB], v2s[R > 2 ? TB : 1];
+  auto kslot = [&](auto ic) ATTN_INLINE -> uint16_t* {
+    constexpr int i = decltype(ic)::value % R;
+    if constexpr (i == 0) return k0s;
+    else if constexpr (i == 1) return k1s;
+    else return k2s;
+  };
+  auto vslot = [&](auto ic) ATTN_INLINE -> uint16_t* {
+    constexpr int i = decltype(ic)::value % R;
+    if constexpr (i == 0) return v0s;
+    else if constexpr (i == 1) return v1s;
+    else return v2s;
+  };
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   const int l32 = lane & 31, hh = lane >> 5;
-  const TileReader<D> TR(lane);
+  const TileReader<D> TRK(lane);
+  const TileReader<D> TRV(lane);
 
   // Logical tile: contiguous per XCD; heavy (late) query blocks first.
   // Unequal lengths (QK): n is the query length, nk the key length; with
@@ -82,12 +104,13 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   const uint32_t head_bytes = (uint32_t)n * D * 2u;
   const uint32_t khead_bytes = (uint32_t)nk * D * 2u;
   const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rk = make_rsrc(K + khead, khead_bytes);
-  const auto rv = make_rsrc(V + khead, khead_bytes);
+  const RsrcWords rk = rsrc_words(K + khead, khead_bytes);
+  const RsrcWords rv = rsrc_words(V + khead, khead_bytes);
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds its query's 8
   // consecutive features per 16-feature step.  Rows past n read as zero.
-  const int qrow = q0 + 32 * w + l32;
+  const int wq0 = q0 + 32 * w;  // first query of this wave
+  const int qrow = wq0 + l32;
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
@@ -107,159 +130,233 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   const int jlo = klo / BC;
   const int ntiles = kend > klo ? (kend + BC - 1) / BC : jlo;
 
+  // Visited tiles by position p = 0 .. P - 1, and units u = 0 .. U - 1
+  // (unit u is half u % 2 of the tile at position u / 2).
+  int P, U;
+  __shared__ uint32_t tlist[SPARSE ? kMaxSparseTiles + 1 : 1];
+  if constexpr (SPARSE) {
+    // Block-sparse: only the key tiles of the blocks this query block may
+    // attend (a workgroup's 128 rows are exactly one mask block row; a
+    // 64-key tile is half of a mask block), listed in LDS first.
+    static_assert(BR == kSparseBlock, "one workgroup per mask block row");
+    int* const tcount = reinterpret_cast<int*>(tlist + kMaxSparseTiles);
+    const uint8_t* mrow = bmask + (size_t)bh * mask_stride + (size_t)qb * nb;
+    P = build_tile_list([&](int j) ATTN_INLINE { return mrow[j >> 1] != 0; }, 0, ntiles, tlist, tcount, w, lane);
+    U = 2 * P;
+  } else {
+    P = ntiles - jlo;
+    U = P > 0 ? (kend - jlo * BC + BU - 1) / BU : 0;
+  }
+  auto tile = [&](int p) ATTN_INLINE {
+    if constexpr (SPARSE)
+      return __builtin_amdgcn_readfirstlane((int)tlist[p]);
+    else
+      return jlo + p;
+  };
+  auto ju = [&](int u) ATTN_INLINE { return tile(u >> 1) * BC + BU * (u & 1); };  // first key of unit u
+  auto active = [&](int j0) ATTN_INLINE { return !CAUSAL || j0 <= wq0 + 31 + coff; };
+  auto need_mask = [&](int j0) ATTN_INLINE { return j0 + BU > khi || (CAUSAL && j0 + BU - 1 > wq0 + coff); };
+
+  // K of position p lives in ring slot p % R, V likewise.  Slots are
+  // compile-time constants: SLOT = p mod R.
+  auto issue_k = [&](auto slot, int p) ATTN_INLINE {
+    if (p < P) dma_tile_asm<D, NW>(rk, kslot(slot), tile(p) * BC, w, lane);
+  };
+  auto issue_v = [&](auto slot, int p) ATTN_INLINE {
+    if (p >= 0 && p < P) dma_tile_asm<D, NW>(rv, vslot(slot), tile(p) * BC, w, lane);
+  };
+  // Fetches issued when tile t opens (t modulo R = TM): K(t + R - 1), V(t + R - 2).
+  auto issue = [&](auto tm, int t) ATTN_INLINE {
+    constexpr int T = decltype(tm)::value;
+    issue_k(std::integral_constant<int, (T + R - 1) % R>{}, t + R - 1);
+    issue_v(std::integral_constant<int, (T + 2 * R - 2) % R>{}, t + R - 2);
+  };
+  // Opening tile t (before step 2t - 1, the first to read K of tile t and V
+  // of tile t - 1): their fetches are complete, every wave is done with the
+  // slots of K(t - 1) and V(t - 2), which the next fetches overwrite.
+  auto handover = [&](auto tm, int t) ATTN_INLINE {
+    if constexpr (R > 2) {
+      if (t + R - 2 < P)
+        wait_vmem_upto<(R - 2) * 2 * IPW>();  // the later batches stay in flight
+      else
+        wait_vmem();
+    } else {
+      wait_vmem();
+    }
+    __syncthreads();
+    issue(tm, t);
+  };
+
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int e = 0; e < D / 32; ++e)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[e][r] = 0.f;
   float mref = -INFINITY;  // reference max (raw score units) used by exp2
+  float mc = 0.f;          // mref * c (0 while mref = -inf)
+  float gate = -1.f;       // a unit sum above this takes the slow path
   float lsum = 0.f;        // this lane's share of the running sum
-  const float tau_raw = kTau / c;
-  const int wq0 = q0 + 32 * w;  // first query of this wave
+  f32x16 s0, s1;           // scores of even / odd units
+  bf16x8 p0[2], p1[2];     // probabilities of even / odd units
 
-  auto compute = [&](const uint16_t* kb, const uint16_t* vb, int j0) {
-    const bool active = !CAUSAL || (j0 <= wq0 + 31 + coff);
-    if (!active) return;
-    f32x16 sacc[2];
+  // One pipeline step: scores of the next unit (tile rows at kb) into sn;
+  // probabilities of this unit (sc -> pn; returns this lane's sum); output
+  // products of the previous unit (po, tile rows at vb).  Straight-line code:
+  // a unit that must not contribute is masked to -inf (probabilities 0, so
+  // its output products add zeros to finite V rows), and the matrix and
+  // vector work can be interleaved freely.
+  auto step = [&](auto has_pv, f32x16& sc, f32x16& sn, bf16x8(&pn)[2], const bf16x8(&po)[2], const uint16_t* kb,
+                  const uint16_t* vb) ATTN_INLINE -> float {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int r = 0; r < 16; ++r) sn[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[t][r] = 0.f;
+    for (int s = 0; s < D / 16; ++s) sn = mfma32(TRK.rows(kb, 0, s), qf[s], sn);
+    // (Step 0 has no previous unit; its V slot holds no data yet.)
+    if constexpr (decltype(has_pv)::value) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      sacc[0] = mfma32(TR.rows(kb, 0, s), qf[s], sacc[0]);
-      sacc[1] = mfma32(TR.rows(kb, 32, s), qf[s], sacc[1]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) oacc[e] = mfma32(TRV.cols(vb, 16 * h, e), po[h], oacc[e]);
     }
-
-    // Mask (diagonal and ragged tiles only) and take this query's tile max.
-    const bool need_mask = (j0 + BC > khi) || (CAUSAL && j0 + BC - 1 > wq0 + coff);
-    if (need_mask) {
+    float p[16], a[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + 32 * t + crow(r, hh);
-          const bool dead = (key >= khi) || (CAUSAL && key > qrow + coff);
-          sacc[t][r] = dead ? -INFINITY : sacc[t][r];
-        }
+    for (int r = 0; r < 16; ++r) {
+      p[r] = fast_exp2(fmaf(sc[r], c, -mc));
+      a[r & 3] = r < 4 ? p[r] : a[r & 3] + p[r];
     }
-    float mx = -INFINITY;
+    pn[0] = pack_bf16x8(p);
+    pn[1] = pack_bf16x8(p + 8);
+    // Keep the conversions here, so the 16 probabilities die in this step.
+    asm volatile("" ::"v"(pn[0]), "v"(pn[1]));
+    // Interleave: each matrix product is preceded by LDS reads for a later
+    // one and followed by a share of the exponential work (masks: 0x100 LDS
+    // read, 0x008 MFMA, 0x402 VALU).
+    constexpr int NP = D / 16;
+    constexpr int VPM = (56 + 2 * NP - 1) / (2 * NP);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-    mx = half_max(mx);
+    for (int i = 0; i < NP; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, VPM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, VPM, 0);
+    }
+    return (a[0] + a[1]) + (a[2] + a[3]);
+  };
 
-    // Raise the reference max only when some row outgrew it by > 2^tau.
-    // Square: tile 0 always holds key 0, which every query may see, so the
-    // reference is finite from the first tile on.  Unequal lengths: a row
-    // may see no key of its first tiles, so its reference can stay -inf;
-    // then nothing is rescaled and its probabilities are 0.
-    if (__builtin_amdgcn_ballot_w64(mx > mref + tau_raw) != 0) {
+  // After a step: if some lane's unit sum exceeds the gate, raise the
+  // reference to the unit's max, rescale, and recompute the unit.
+  auto settle = [&](f32x16& sc, bf16x8(&pn)[2], float ps) ATTN_INLINE {
+    if (__builtin_amdgcn_ballot_w64(ps > gate) != 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+      mx = half_max(mx);
       const float m_new = fmaxf(mref, mx);
-      const float alpha = (QK && m_new == -INFINITY) ? 1.f : fast_exp2((mref - m_new) * c);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2((mref - m_new) * c);
       mref = m_new;
+      mc = m_new == -INFINITY ? 0.f : m_new * c;
+      gate = m_new == -INFINITY ? -1.f : kGate;
       lsum *= alpha;
 #pragma unroll
       for (int e = 0; e < D / 32; ++e)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[e][r] *= alpha;
-    }
-    const float mc = (QK && mref == -INFINITY) ? 0.f : mref * c;
-
-    bf16x8 pf[2][2];
+      float p[16];
+      ps = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float p[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = fast_exp2(fmaf(sacc[t][8 * u + i], c, -mc));
-          lsum += p[i];
-        }
-        pf[t][u] = pack_bf16x8(p);
+      for (int r = 0; r < 16; ++r) {
+        p[r] = fast_exp2(fmaf(sc[r], c, -mc));
+        ps += p[r];
       }
-
-    // O^T += V^T P^T over the 64 keys of the tile.
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < D / 32; ++e)
-          oacc[e] = mfma32(TR.cols(vb, 32 * t + 16 * u, e), pf[t][u], oacc[e]);
+      pn[0] = pack_bf16x8(p);
+      pn[1] = pack_bf16x8(p + 8);
+    }
+    lsum += ps;
   };
 
-  if constexpr (SPARSE) {
-    // Block-sparse: only the key tiles of the blocks this query block may
-    // attend are fetched and computed (a workgroup's 128 rows are exactly one
-    // mask block row; a 64-key tile is half of a mask block).  Their indices
-    // are listed in LDS first, then walked like the dense sequence.
-    static_assert(BR == kSparseBlock, "one workgroup per mask block row");
-    __shared__ uint32_t tlist[kMaxSparseTiles];
-    __shared__ int tcount;
-    const uint8_t* mrow = bmask + (size_t)bh * mask_stride + (size_t)qb * nb;
-    const int cnt = build_tile_list([&](int j) ATTN_INLINE { return mrow[j >> 1] != 0; }, 0, ntiles, tlist, &tcount,
-                                    w, lane);
-    auto tile = [&](int p) ATTN_INLINE { return __builtin_amdgcn_readfirstlane((int)tlist[p]); };
-    if (cnt > 0) {
-      dma_tile<D, NW>(rk, k0s, tile(0) * BC, w, lane);
-      dma_tile<D, NW>(rv, v0s, tile(0) * BC, w, lane);
-      wait_vmem();
-      __syncthreads();
-    }
-    for (int p = 0; p < cnt; p += 2) {
-      if (p + 1 < cnt) {
-        dma_tile<D, NW>(rk, k1s, tile(p + 1) * BC, w, lane);
-        dma_tile<D, NW>(rv, v1s, tile(p + 1) * BC, w, lane);
+  // Step u (u = 0 .. U; step U only ends the output products of unit U - 1),
+  // with k = u modulo 2R so that every ring slot is a compile-time offset.
+  // Units that need a mask (diagonal, ragged, past the end) are masked in
+  // place first; a causal step whose units all lie above this wave's rows is
+  // skipped.
+  auto run_step = [&](auto kc, int u) ATTN_INLINE {
+    constexpr int k = decltype(kc)::value;
+    constexpr bool ODD = k & 1;
+    constexpr int half = ((k + 1) & 1) * BU * D;                           // of units u + 1 and u - 1
+    const uint16_t* kb = kslot(std::integral_constant<int, ((k + 1) >> 1)>{}) + half;           // unit u + 1
+    const uint16_t* vb = vslot(std::integral_constant<int, ((k + 2 * R - 1) >> 1)>{}) + half;  // unit u - 1
+    auto go = [&](f32x16& sc, f32x16& sn, bf16x8(&pn)[2], const bf16x8(&po)[2]) ATTN_INLINE {
+      const int j0 = u < U ? ju(u) : khi;
+      if (CAUSAL && u >= 1 && !active(ju(u - 1))) return;
+      if (need_mask(j0)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j0 + crow(r, hh);
+          const bool dead = (key >= khi) || (CAUSAL && key > qrow + coff);
+          sc[r] = dead ? -INFINITY : sc[r];
+        }
       }
-      compute(k0s, v0s, tile(p) * BC);
-      wait_vmem();
-      __syncthreads();
-      if (p + 1 >= cnt) break;
-      if (p + 2 < cnt) {
-        dma_tile<D, NW>(rk, k0s, tile(p + 2) * BC, w, lane);
-        dma_tile<D, NW>(rv, v0s, tile(p + 2) * BC, w, lane);
-      }
-      compute(k1s, v1s, tile(p + 1) * BC);
-      wait_vmem();
-      __syncthreads();
+      const float ps = step(std::bool_constant<(k > 0)>{}, sc, sn, pn, po, kb, vb);
+      settle(sc, pn, ps);
+    };
+    if constexpr (ODD)
+      go(s1, s0, p1, p0);
+    else
+      go(s0, s1, p0, p1);
+  };
+
+  if (P > 0) {
+    issue_k(std::integral_constant<int, 0>{}, 0);
+    if constexpr (R > 2) issue(std::integral_constant<int, R - 1>{}, -1);
+    issue(std::integral_constant<int, 0>{}, 0);
+    if constexpr (R > 1) {
+      if (R - 1 < P)
+        wait_vmem_upto<(R - 1) * 2 * IPW>();  // K of tile 0 has arrived
+      else
+        wait_vmem();
     }
-  } else {
-  if (!QK || jlo < ntiles) {
-    dma_tile<D, NW>(rk, k0s, jlo * BC, w, lane);
-    dma_tile<D, NW>(rv, v0s, jlo * BC, w, lane);
-    wait_vmem();
     __syncthreads();
   }
 
-  for (int jt = jlo; jt < ntiles; jt += 2) {
-    // Even tile from buffer 0; tile jt+1 streams into buffer 1.
-    if (jt + 1 < ntiles) {
-      dma_tile<D, NW>(rk, k1s, (jt + 1) * BC, w, lane);
-      dma_tile<D, NW>(rv, v1s, (jt + 1) * BC, w, lane);
+  if (U > 0) {
+    // Scores of unit 0, then the steps; step u > 0 ends the output products
+    // of unit u - 1, so the last one is step U.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s0[r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) s0 = mfma32(TRK.rows(k0s, 0, s), qf[s], s0);
+    run_step(std::integral_constant<int, 0>{}, 0);
+    int u = 1;
+    bool run = true;
+    while (run) {
+      auto body = [&](auto kc) ATTN_INLINE {
+        constexpr int k = decltype(kc)::value;
+        if (!run || u > U) {
+          run = false;
+          return;
+        }
+        if constexpr (k & 1) handover(std::integral_constant<int, (((k + 1) >> 1) % R)>{}, (u + 1) >> 1);
+        run_step(kc, u);
+        ++u;
+      };
+      body(std::integral_constant<int, 1>{});
+      body(std::integral_constant<int, 2>{});
+      body(std::integral_constant<int, 3>{});
+      body(std::integral_constant<int, 4>{});
+      if constexpr (R > 2) {
+        body(std::integral_constant<int, 5>{});
+        body(std::integral_constant<int, 6>{});
+      }
     }
-    compute(k0s, v0s, jt * BC);
-    wait_vmem();
-    __syncthreads();
-    if (jt + 1 >= ntiles) break;
-    // Odd tile from buffer 1; tile jt+2 streams into buffer 0.
-    if (jt + 2 < ntiles) {
-      dma_tile<D, NW>(rk, k0s, (jt + 2) * BC, w, lane);
-      dma_tile<D, NW>(rv, v0s, (jt + 2) * BC, w, lane);
-    }
-    compute(k1s, v1s, (jt + 1) * BC);
-    wait_vmem();
-    __syncthreads();
-  }
   }
 
   // Epilogue: O = acc / l (bf16, nearest-even), LSE = (m c + log2 l) ln 2.
   // Rows that may attend no key (block-sparse, unequal lengths, or a split
   // with none of the row's keys) have l = 0: O = 0 and LSE = -inf.
   const float ltot = half_sum(lsum);
-  const bool empty = (SPARSE || QK) && ltot == 0.f;
+  const bool empty = ltot == 0.f;
   const float inv = empty ? 0.f : 1.0f / ltot;
   const float lse_v = empty ? -INFINITY : (mref * c + fast_log2(ltot)) * kLn2;
   if (QK && nsplit > 1) {

@@ -53,11 +53,20 @@ __device__ __forceinline__ void wait_vmem_upto() {
 
 // DMA rows [row0, row0 + 64) of a [n, D] bf16 matrix (buffer `rs`) into the
 // LDS tile at `lds`.  The NW waves of the workgroup split the 64 rows.
+// Load k (k = 0 .. D/8 - 1) fills LDS bytes 1024k .. 1024k + 1023, lane i the
+// 16 bytes at 1024k + 16i, so each lane fetches the global chunk that belongs
+// there.  Its byte offset within the tile is 1024k + (b ^ x(k)): b is load
+// 0's offset for the lane and x(k) the part of the swizzle that varies with k
+// (16 (k % 4) at D = 128, 32 (k % 2) at D = 64).
 template <int D, int NW>
 __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* lds, int row0, int w, int lane) {
   constexpr int CPR = D / 8;      // 16-byte chunks per row
   constexpr int IPW = CPR / NW;   // 1 KiB loads per wave
   static_assert(IPW >= 1 && IPW * NW == CPR, "waves must split the tile evenly");
+  // One long-lived register per lane; the copy is opaque, so the per-load
+  // offsets are formed here rather than kept in registers across loops.
+  uint32_t b = tile_off<D>(lane / CPR, lane % CPR);
+  asm volatile("" : "+v"(b));
   // The tile's byte offset goes through readfirstlane: opaque to loop
   // strength reduction, which would otherwise keep one address vector per
   // load and buffer alive across the tile loop.
@@ -65,11 +74,52 @@ __device__ __forceinline__ void dma_tile(__amdgpu_buffer_rsrc_t rs, uint16_t* ld
 #pragma unroll
   for (int r = 0; r < IPW; ++r) {
     const int k = w * IPW + r;
-    const int p = 64 * k + lane;          // LDS chunk this lane fills
-    const int row = p / CPR, cp = p % CPR;
-    const int c = cp ^ tile_swz<D>(row);  // global chunk that belongs there
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(lds + 512 * k), 16,
-                                             base + (uint32_t)(row * (D * 2) + 16 * c), 0, 0, 0);
+    const uint32_t xk = D == 128 ? 16u * (k & 3) : 32u * (k & 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (ATTN_LDS void*)(lds + 512 * k), 16, base + 1024u * k + (b ^ xk),
+                                             0, 0, 0);
+  }
+}
+
+// The same fetch issued through inline assembly, invisible to the compiler's
+// LDS-DMA tracking.  The compiler cannot always tell an LDS read of one tile
+// from a fetch in flight into another (it then waits for every fetch before
+// the read, which serialises a software pipeline); kernels using this form
+// wait for their fetches themselves (wait_vmem* before the barrier that
+// hands a tile over).  `words` is the buffer descriptor of make_rsrc as four
+// 32-bit words, so it can live in scalar registers of the asm operand.
+struct RsrcWords {
+  u32x4 w;
+};
+__device__ __forceinline__ RsrcWords rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  RsrcWords r;
+  r.w[0] = (uint32_t)a;
+  r.w[1] = (uint32_t)(a >> 32) & 0xFFFFu;  // stride 0
+  r.w[2] = bytes;
+  r.w[3] = 0x00020000u;
+  return r;
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile_asm(const RsrcWords& rs, uint16_t* lds, int row0, int w, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int IPW = CPR / NW;
+  static_assert(IPW >= 1 && IPW * NW == CPR, "waves must split the tile evenly");
+  uint32_t b = tile_off<D>(lane / CPR, lane % CPR);
+  asm volatile("" : "+v"(b));
+  const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)row0 * (D * 2));
+  const uint32_t l0 = (uint32_t)(uintptr_t)(ATTN_LDS uint16_t*)lds;
+#pragma unroll
+  for (int r = 0; r < IPW; ++r) {
+    const int k = w * IPW + r;
+    const uint32_t xk = D == 128 ? 16u * (k & 3) : 32u * (k & 1);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(l0 + 1024u * k);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(m0), "v"(base + 1024u * k + (b ^ xk)), "s"(rs.w)
+        : "memory", "m0");
   }
 }
 
