@@ -152,10 +152,13 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   const size_t head = (size_t)bh * (size_t)n * D;
   const size_t khead = (size_t)bh * (size_t)nk * D;
   const uint32_t head_bytes = (uint32_t)n * D * 2u;
-  const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rdo = make_rsrc(dO + head, head_bytes);
-  const auto rl = make_rsrc(LSE + (size_t)bh * n, (uint32_t)n * 4u);
-  const auto rd = make_rsrc(Dsum + (size_t)bh * n, (uint32_t)n * 4u);
+  // Q and dO tiles are fetched through inline asm (dma_tile_asm): the
+  // compiler would otherwise make LDS accesses of one buffer wait for the
+  // fetch in flight into another; the waits it needs are explicit here.
+  const RsrcWords rq = rsrc_words(Q + head, head_bytes);
+  const RsrcWords rdo = rsrc_words(dO + head, head_bytes);
+  const RsrcWords rl = rsrc_words(LSE + (size_t)bh * n, (uint32_t)n * 4u);
+  const RsrcWords rd = rsrc_words(Dsum + (size_t)bh * n, (uint32_t)n * 4u);
 
   // B operands of S (K rows) for the S wave, of dP (V rows) for the dP wave.
   bf16x8 bf[D / 16];
@@ -163,6 +166,9 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     const auto rkv = make_rsrc((s_role ? K : V) + khead, (uint32_t)nk * D * 2u);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) bf[s] = as_bf16x8(bload16(rkv, (uint32_t)key * (D * 2) + 32 * s + 16 * hh));
+    // Complete before any tile fetch is issued: a wait for these registers
+    // inside the tile loop would also wait for the fetches in flight.
+    wait_vmem();
   }
 
   f32x16 acc[D / 32];  // dV^T (S wave) or dK^T (dP wave)
@@ -192,32 +198,37 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 
   // Query rows past n load as zero (Q, dO, LSE, D), so they contribute
   // nothing: P = 1 is finite and multiplies dO = 0 and dS = 0.
-  float lr = 0.f, dr = 0.f;
-  auto load_small = [&](int i) ATTN_INLINE {
-    if (tid < BQ) {
-      const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)i * (BQ * 4)) + (uint32_t)tid * 4u;
-      lr = bload4f(rl, off) * kLog2e;
-      dr = bload4f(rd, off);
-    }
-  };
-  auto store_small = [&](auto b) ATTN_INLINE {
-    if (tid < BQ) {
-      lse_at(b)[tid] = lr;
-      dsm_at(b)[tid] = dr;
-    }
-  };
+  // A tile's batch of fetches: LSE and D rows (wave 0, one load each), then
+  // the Q and dO tiles (2 * IPW loads per wave).  Every tile issues the same
+  // batch (past the last tile: copies of the last one, never read), so the
+  // counts below hold on every path.
+  constexpr int SMALLN = 2;  // LSE and D loads of wave 0
   auto dma = [&](int i, auto b) ATTN_INLINE {
-    dma_tile<D, NW>(rq, q_at(b), i * BQ, w, lane);
-    dma_tile<D, NW>(rdo, g_at(b), i * BQ, w, lane);
+    if (w == 0) {
+      const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)i * (BQ * 4));
+      dma_row64_asm(rl, lse_at(b), off, lane);
+      dma_row64_asm(rd, dsm_at(b), off, lane);
+    }
+    dma_tile_asm<D, NW>(rq, q_at(b), i * BQ, w, lane);
+    dma_tile_asm<D, NW>(rdo, g_at(b), i * BQ, w, lane);
   };
-  // End of a tile: the DMA of the next tile must have landed; the one of
-  // the tile after it (2 * IPW loads, issued last) may still be in flight.
-  auto handover = [&](bool more) ATTN_INLINE {
-    if (more)
-      wait_vmem_upto<2 * IPW>();
+  // Wave 0 scales the landed LSE row of buffer b to base 2, in place; the
+  // tiles fetched after it (LATER loads) may still be in flight.
+  auto fix_small = [&](auto b, auto later) ATTN_INLINE {
+    if (w == 0) {
+      wait_vmem_upto<decltype(later)::value>();
+      asm volatile("" ::: "memory");
+      lse_at(b)[lane] *= kLog2e;
+    }
+  };
+  // End of a tile: the batch of the next tile must have landed; the batch
+  // of the tile after it (issued last) stays in flight.
+  auto handover = [&]() ATTN_INLINE {
+    if (w == 0)
+      wait_vmem_upto<SMALLN + 2 * IPW>();
     else
-      wait_vmem();
-    __syncthreads();
+      wait_vmem_upto<2 * IPW>();
+    barrier_lds();
   };
 
   float* px = pxs + grp * (2 * 4 * 64 * 4);
@@ -273,19 +284,17 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   auto run_dense = [&](auto&& body) ATTN_INLINE {
     auto step = [&](auto b, int i) ATTN_INLINE {
       constexpr int B = decltype(b)::value;
-      if (i + 1 < ntq) load_small(i + 1);
       body(b, i, [&]() ATTN_INLINE {
-        __syncthreads();  // P of tile i is published; reads of tile i - 1 are done
-        if (i + 2 < ntq) dma(i + 2, int_c<(B + 2) % 3>{});
+        fix_small(int_c<(B + 1) % 3>{}, int_c<2 * IPW>{});  // LSE of tile i + 1
+        barrier_lds();  // P of tile i is published; reads of tile i - 1 are done
+        dma(min(i + 2, ntq - 1), int_c<(B + 2) % 3>{});
       });
-      if (i + 1 < ntq) store_small(int_c<(B + 1) % 3>{});
-      handover(i + 2 < ntq);
+      handover();
     };
-    load_small(it0);
     dma(it0, int_c<0>{});
-    if (it0 + 1 < ntq) dma(it0 + 1, int_c<1>{});
-    store_small(int_c<0>{});
-    handover(it0 + 1 < ntq);
+    dma(min(it0 + 1, ntq - 1), int_c<1>{});
+    fix_small(int_c<0>{}, int_c<SMALLN + 4 * IPW>{});
+    handover();
     for (int it = it0; it < ntq; it += 3) {
       step(int_c<0>{}, it);
       if (it + 1 >= ntq) break;
@@ -300,20 +309,18 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     auto T = [&](int p) ATTN_INLINE { return __builtin_amdgcn_readfirstlane((int)tlist[p]); };
     auto step = [&](auto b, int p) ATTN_INLINE {
       constexpr int B = decltype(b)::value;
-      if (p + 1 < tcnt) load_small(T(p + 1));
       body(b, T(p), [&]() ATTN_INLINE {
-        __syncthreads();  // P of this tile is published; reads of the previous one are done
-        if (p + 2 < tcnt) dma(T(p + 2), int_c<(B + 2) % 3>{});
+        fix_small(int_c<(B + 1) % 3>{}, int_c<2 * IPW>{});  // LSE of the next tile
+        barrier_lds();  // P of this tile is published; reads of the previous one are done
+        dma(T(min(p + 2, tcnt - 1)), int_c<(B + 2) % 3>{});
       });
-      if (p + 1 < tcnt) store_small(int_c<(B + 1) % 3>{});
-      handover(p + 2 < tcnt);
+      handover();
     };
     if (tcnt == 0) return;
-    load_small(T(0));
     dma(T(0), int_c<0>{});
-    if (tcnt > 1) dma(T(1), int_c<1>{});
-    store_small(int_c<0>{});
-    handover(tcnt > 1);
+    dma(T(min(1, tcnt - 1)), int_c<1>{});
+    fix_small(int_c<0>{}, int_c<SMALLN + 4 * IPW>{});
+    handover();
     for (int p = 0; p < tcnt; p += 3) {
       step(int_c<0>{}, p);
       if (p + 1 >= tcnt) break;
@@ -327,6 +334,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
       run_list(body);
     else
       run_dense(body);
+    wait_vmem();  // no fetch outlives the loop
   };
 
   if (s_role) {

@@ -51,6 +51,20 @@ __device__ __forceinline__ void wait_vmem_upto() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Workgroup barrier for LDS hand-overs that leaves vector-memory operations
+// (tile fetches into LDS among them) in flight: this wave's LDS reads and
+// writes are complete (lgkmcnt 0), then s_barrier.  __syncthreads() would
+// also wait for every outstanding fetch (its release fence waits vmcnt 0),
+// which defeats fetching a tile more than one tile ahead.  Callers wait for
+// the fetches they need (wait_vmem_upto) before the barrier; the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // DMA rows [row0, row0 + 64) of a [n, D] bf16 matrix (buffer `rs`) into the
 // LDS tile at `lds`.  The NW waves of the workgroup split the 64 rows.
 // Load k (k = 0 .. D/8 - 1) fills LDS bytes 1024k .. 1024k + 1023, lane i the
@@ -121,6 +135,18 @@ __device__ __forceinline__ void dma_tile_asm(const RsrcWords& rs, uint16_t* lds,
         : "s"(m0), "v"(base + 1024u * k + (b ^ xk)), "s"(rs.w)
         : "memory", "m0");
   }
+}
+
+// 64 consecutive fp32 values (one per lane: bytes 4 * lane) into LDS at
+// `lds`, through the same invisible path.
+__device__ __forceinline__ void dma_row64_asm(const RsrcWords& rs, float* lds, uint32_t byte_off, int lane) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS float*)lds);
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "buffer_load_dword %1, %2, 0 offen lds"
+      :
+      : "s"(m0), "v"(byte_off + 4u * (uint32_t)lane), "s"(rs.w)
+      : "memory", "m0");
 }
 
 // Per-lane LDS byte offsets for reading MFMA operand fragments from tiles in
