@@ -46,7 +46,7 @@
 namespace attn {
 
 template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK>
-__global__ __launch_bounds__(NW * 64, 8 / NW) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
                                                                    const uint16_t* __restrict__ K,
                                                                    const uint16_t* __restrict__ V,
                                                                    uint16_t* __restrict__ O,
