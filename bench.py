@@ -7,6 +7,9 @@ the forward kernel (O, LSE), then the backward phases D = rowsum(dO * O),
 dK/dV and dQ.  Inputs are resident in HBM before the timed region starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       (without --no-cpu the line also carries two CPU references on bounded
+       samples of the workload: the float64 oracle, cpu_baseline, and the
+       cache-blocked CPU implementation of libattn_cpu.so, cpu_flash)
        python bench.py --sweep           (one JSON line per N, d, mask, pass)
        python bench.py --blocksparse     (block-sparse vs dense, one JSON line
                                           per block density and mask)
@@ -128,6 +131,38 @@ def cpu_baseline(shape, budget_s=12.0, max_heads=256):
         "kind": "oracle",
         "sample": f"{heads} (batch, head) slices of N={n} d={d}, alternating full/causal mask, "
         f"forward + backward in float64 ({dt:.1f} s, {flops / 1e9:.0f} GFLOP by the same convention)",
+    }
+
+
+def cpu_flash(shape, budget_s=8.0, max_heads=64):
+    """The cache-blocked multi-core CPU form of the method (libattn_cpu.so) on
+    a bounded sample of the same workload: (batch, head) slices of the same
+    shape, alternating full/causal mask, forward + backward, all host threads."""
+    import synth
+    from exact_io_aware_05_amd import cpu as C
+
+    b, h, n, d = shape
+    inp = synth.qkvdo(3, (1, 2, n, d), "bf16")
+    q, k, v, do = (inp[x].astype(np.float32) for x in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(d)
+    C.attn_cpu_fwd(q[:, :1, :64], k[:, :1, :64], v[:, :1, :64])  # load the library, start the threads
+    flops, heads = 0.0, 0
+    t0 = time.perf_counter()
+    while heads < max_heads and (time.perf_counter() - t0) < budget_s:
+        causal = heads % 2 == 1
+        sl = slice(heads % 2, heads % 2 + 1)
+        o, lse = C.attn_cpu_fwd(q[:, sl], k[:, sl], v[:, sl], causal, scale)
+        C.attn_cpu_bwd(q[:, sl], k[:, sl], v[:, sl], o, do[:, sl], lse, causal, scale)
+        flops += 3.5 * fwd_flops(1, n, d, causal)
+        heads += 1
+    dt = time.perf_counter() - t0
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(os.environ.get("OMP_NUM_THREADS") or len(os.sched_getaffinity(0))),
+        "kind": "cache-blocked CPU implementation (fp32, OpenMP)",
+        "sample": f"{heads} (batch, head) slices of N={n} d={d}, alternating full/causal mask, "
+        f"forward + backward ({dt:.1f} s)",
     }
 
 
@@ -320,6 +355,7 @@ def main():
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(shape)
+        out["cpu_flash"] = cpu_flash(shape)
     print(json.dumps(out), flush=True)
 
 

@@ -17,6 +17,10 @@ Entry points carry the C names:
   lengths (bottom-right causal alignment), with split-K/V for the forward
 * :func:`attn_bwd_workspace_bytes`, :func:`attn_status_string`
 * :func:`lib` -- the raw ``ctypes.CDLL``.
+
+The cache-blocked multi-core CPU form of the same attention is a separate
+library with its own binding, :mod:`exact_io_aware_05_amd.cpu`; nothing here
+calls it.
 """
 
 import ctypes

@@ -1,8 +1,10 @@
-"""Build the HIP attention library (``libattn.so``) for gfx950 with hipcc.
+"""Build the HIP attention library (``libattn.so``) for gfx950 with hipcc, and
+the CPU library (``libattn_cpu.so``) with g++.
 
 Run as ``python -m exact_io_aware_05_amd.build``.  Each ``csrc/*.hip`` file is
 compiled to an object in ``_build/`` (in parallel), then linked in-tree to
-``exact_io_aware_05_amd/libattn.so``.
+``exact_io_aware_05_amd/libattn.so``; ``csrc/attn_cpu.cpp`` becomes
+``exact_io_aware_05_amd/libattn_cpu.so``.
 """
 
 import concurrent.futures
@@ -33,8 +35,26 @@ COMMON = [
 ] + DEVICE_FLAGS
 
 
+CPU_LIB = os.path.join(PKG, "libattn_cpu.so")
+CXX = os.environ.get("CXX", "g++")
+# The CPU library (include/attn_cpu.h): AVX2 + FMA, which every x86-64 host of
+# an MI355X supports, and OpenMP.
+CPU_FLAGS = ["-O3", "-mavx2", "-mfma", "-fopenmp", "-fPIC", "-shared", "-std=c++17", "-Wall", "-Wextra"]
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+
+
+def build_cpu():
+    """Compile csrc/attn_cpu.cpp into exact_io_aware_05_amd/libattn_cpu.so."""
+    tmp = CPU_LIB + ".tmp"
+    cmd = [CXX] + CPU_FLAGS + ["-I", os.path.join(ROOT, "include"), os.path.join(CSRC, "attn_cpu.cpp"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed for attn_cpu.cpp:\n{r.stderr}")
+    os.replace(tmp, CPU_LIB)
+    return CPU_LIB
 
 
 def _compile(src):
@@ -64,6 +84,7 @@ def build(verbose=False):
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_cpu()
     return LIB
 
 

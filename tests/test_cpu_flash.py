@@ -1,0 +1,102 @@
+"""The cache-blocked multi-core CPU form of the method (include/attn_cpu.h,
+libattn_cpu.so) against the float64 oracle.
+
+The CPU library computes in float32 from bf16-valued inputs (exact in
+float32), so its results must match the oracle to float32 accumulation error:
+1e-4 absolute here (observed about 3e-6).  It runs on the host, so these tests
+belong to the CPU suite.
+"""
+
+import ctypes
+import math
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import attention as A
+
+TOL = 1e-4
+
+
+def _cpu():
+    from exact_io_aware_05_amd import cpu as C
+
+    if not os.path.exists(C.CPU_LIB_PATH):
+        pytest.skip("libattn_cpu.so not built")
+    C.lib()
+    return C
+
+
+CASES = [
+    # (B, H, N, d): one key tile, several tiles with a ragged tail, one row, odd d
+    (1, 2, 64, 64),
+    (2, 2, 200, 64),
+    (1, 3, 130, 128),
+    (1, 1, 1, 128),
+    (1, 2, 77, 48),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", CASES)
+def test_forward_and_backward_match_the_oracle(shape, causal):
+    C = _cpu()
+    inp = synth.qkvdo(900 + shape[2] + shape[3], shape, "bf16")
+    scale = 1.0 / math.sqrt(shape[3])
+    o, lse = C.attn_cpu_fwd(inp["q"], inp["k"], inp["v"], causal, scale)
+    dq, dk, dv = C.attn_cpu_bwd(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, causal, scale)
+    o_r, lse_r = A.forward(inp["q"], inp["k"], inp["v"], causal, scale)
+    g_r = A.backward(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale)
+    for name, got, ref in (("O", o, o_r), ("LSE", lse, lse_r), ("dQ", dq, g_r[0]), ("dK", dk, g_r[1]),
+                           ("dV", dv, g_r[2])):
+        err = float(np.max(np.abs(got.astype(np.float64) - ref)))
+        assert err <= TOL, f"{name}: max abs {err:.3e}"
+
+
+def test_scale_other_than_default():
+    C = _cpu()
+    shape = (1, 2, 150, 64)
+    inp = synth.qkvdo(77, shape, "bf16")
+    o, lse = C.attn_cpu_fwd(inp["q"], inp["k"], inp["v"], True, 0.05)
+    o_r, lse_r = A.forward(inp["q"], inp["k"], inp["v"], True, 0.05)
+    assert np.max(np.abs(o - o_r)) <= TOL and np.max(np.abs(lse - lse_r)) <= TOL
+
+
+def test_result_does_not_depend_on_the_thread_count():
+    # Each work item is computed by one thread in a fixed order.
+    C = _cpu()
+    shape = (2, 2, 300, 64)
+    inp = synth.qkvdo(78, shape, "bf16")
+    a = C.attn_cpu_fwd(inp["q"], inp["k"], inp["v"], True, threads=1)
+    b = C.attn_cpu_fwd(inp["q"], inp["k"], inp["v"], True, threads=3)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    ga = C.attn_cpu_bwd(inp["q"], inp["k"], inp["v"], a[0], inp["do"], a[1], True, threads=1)
+    gb = C.attn_cpu_bwd(inp["q"], inp["k"], inp["v"], a[0], inp["do"], a[1], True, threads=4)
+    assert all(np.array_equal(x, y) for x, y in zip(ga, gb))
+
+
+def test_header_declares_what_the_library_exports():
+    C = _cpu()
+    import re
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(root, "include", "attn_cpu.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(attn_cpu_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["attn_cpu_bwd", "attn_cpu_fwd"]
+    for nm in names:
+        assert hasattr(C.lib(), nm)
+
+
+def test_invalid_arguments_are_rejected():
+    C = _cpu()
+    L = C.lib()
+    buf = np.zeros(64 * 64, dtype=np.float32)
+    p = buf.ctypes.data_as(ctypes.c_void_p)
+    assert L.attn_cpu_fwd(None, p, p, p, p, 1, 1, 16, 64, 0, 0.1, 1) == -1
+    assert L.attn_cpu_fwd(p, p, p, p, p, 1, 0, 16, 64, 0, 0.1, 1) == -2
+    assert L.attn_cpu_fwd(p, p, p, p, p, 1, 1, 16, 300, 0, 0.1, 1) == -3
+    assert L.attn_cpu_fwd(p, p, p, p, p, 1, 1, 16, 64, 0, float("nan"), 1) == -4
+    assert L.attn_cpu_bwd(p, p, p, p, p, p, p, p, None, 1, 1, 16, 64, 0, 0.1, 1) == -1
+    assert L.attn_cpu_bwd(p, p, p, p, p, p, p, p, p, 1, 1, 0, 64, 0, 0.1, 1) == -2
