@@ -31,10 +31,18 @@ Modules:
 * :mod:`oracle.varlen` -- unequal query and key lengths (bottom-right causal
   alignment) and the split-K/V merge by the two-block rule of "Tiling:
   Block-by-Block Softmax".
+* :mod:`oracle.dropout` -- dropout on the probabilities (an element-wise op
+  that "Background" on the Paper Notes page lists among those kernel fusion
+  folds in), with the mask from the Philox4x32-10 counter-based generator.
 
 Every function here is pinned by ``tests/test_oracle*.py`` against page-printed
-values, closed forms, invariants, finite differences and a library autograd;
-no function is "parity unpinned".
+values, closed forms, invariants, finite differences and a library autograd.
+One narrow exception: that ``oracle.dropout.philox4x32_10`` reproduces the
+published generator bit for bit is not pinned by a stored reference stream
+(no such stream is on the pages); its pins are the properties a counter-based
+generator must have (bijection, uniform bits, avalanche, keep rates).  This
+is "parity unpinned" for the generator's identity only; GPU masks are
+compared with the oracle's bit for bit.
 """
 
 from . import attention, online  # noqa: F401
