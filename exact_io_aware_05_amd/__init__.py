@@ -15,6 +15,8 @@ Entry points carry the C names:
   with a block mask over 128 x 128 blocks of the score matrix
 * :func:`attn_fwd_qk`, :func:`attn_bwd_qk` -- queries and keys of different
   lengths (bottom-right causal alignment), with split-K/V for the forward
+* :func:`attn_fwd_dropout`, :func:`attn_bwd_dropout` -- the same with dropout
+  on the probabilities (mask from a counter-based generator, not stored)
 * :func:`attn_bwd_workspace_bytes`, :func:`attn_status_string`
 * :func:`lib` -- the raw ``ctypes.CDLL``.
 
@@ -38,6 +40,8 @@ __all__ = [
     "SPARSE_BLOCK",
     "attn_fwd_qk",
     "attn_bwd_qk",
+    "attn_fwd_dropout",
+    "attn_bwd_dropout",
     "attn_bwd_workspace_bytes",
     "attn_status_string",
     "lib",
@@ -104,6 +108,12 @@ def lib():
     L.attn_bwd_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, i32, f32, vp,
                               ctypes.c_size_t, vp]
     L.attn_bwd_qk.restype = i32
+    u64 = ctypes.c_uint64
+    L.attn_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32, u64, u64, vp]
+    L.attn_fwd_dropout.restype = i32
+    L.attn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32, u64,
+                                   u64, vp, ctypes.c_size_t, vp]
+    L.attn_bwd_dropout.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -404,4 +414,54 @@ def attn_bwd_qk(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, g
     )
     if st != 0:
         raise AttnError(st, "attn_bwd_qk")
+    return dq, dk, dv
+
+
+def attn_fwd_dropout(q, k, v, p_drop, seed, offset=0, causal=False, scale=None, out=None, lse=None):
+    """Forward with dropout on the probabilities; returns (o, lse).  bf16 only.
+
+    The keep mask is a function of (seed, offset, head, query, key); pass the
+    same values to :func:`attn_bwd_dropout`."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v)], q.shape, q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = lib().attn_fwd_dropout(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, _dtype_code(q),
+        int(bool(causal)), float(scale), float(p_drop), int(seed), int(offset), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_fwd_dropout")
+    return out, lse
+
+
+def attn_bwd_dropout(q, k, v, o, do, lse, p_drop, seed, offset=0, causal=False, scale=None, workspace=None,
+                     grads=None):
+    """Backward of :func:`attn_fwd_dropout` (same p_drop, seed, offset, causal,
+    scale); returns (dq, dk, dv)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v), ("o", o), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    st = lib().attn_bwd_dropout(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), B, H, N, d, code, int(bool(causal)), float(scale), float(p_drop), int(seed),
+        int(offset), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_bwd_dropout")
     return dq, dk, dv

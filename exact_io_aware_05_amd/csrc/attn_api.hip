@@ -92,6 +92,21 @@ int check_qk(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype)
   return ATTN_OK;
 }
 
+// Dropout arguments: p in [0, 1) (NaN fails the test); the keep threshold
+// and the scale of kept probabilities.
+int check_dropout(float p) { return (p >= 0.f && p < 1.f) ? ATTN_OK : ATTN_E_DROPOUT; }
+
+attn::DropArgs make_drop(float p, uint64_t seed, uint64_t offset) {
+  attn::DropArgs dr;
+  const double t = floor((double)p * 4294967296.0);
+  dr.thr = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  dr.keep_scale = 1.0f / (1.0f - p);
+  dr.seed_lo = (uint32_t)seed;
+  dr.seed_hi = (uint32_t)(seed >> 32);
+  dr.offset = (uint32_t)offset;
+  return dr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -105,6 +120,7 @@ const char* attn_status_string(int status) {
     case ATTN_E_SCALE: return "scale must be finite";
     case ATTN_E_WORKSPACE: return "workspace missing or too small";
     case ATTN_E_HIP: return "HIP kernel launch failed";
+    case ATTN_E_DROPOUT: return "dropout probability must lie in [0, 1)";
     default: return "unknown status";
   }
 }
@@ -234,6 +250,57 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
       make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
   a.bmask = block_mask;
   a.mask_stride = mask_head_stride;
+  if (attn::bwd_dsum(a, true) != hipSuccess) return ATTN_E_HIP;
+  if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
+  if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
+}
+
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int dtype, int causal, float scale, float p_drop, uint64_t seed,
+                     uint64_t offset, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  st = check_dropout(p_drop);
+  if (st != ATTN_OK) return st;
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = B * H;
+  a.n = N;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  a.dropout = true;
+  a.drop = make_drop(p_drop, seed, offset);
+  return attn::fwd_bf16(a) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal,
+                     float scale, float p_drop, uint64_t seed, uint64_t offset, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  st = check_dropout(p_drop);
+  if (st != ATTN_OK) return st;
+  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, dtype) ||
+      ((uintptr_t)workspace & 255) != 0)
+    return ATTN_E_WORKSPACE;
+  attn::BwdArgs a =
+      make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
+  a.dropout = true;
+  a.drop = make_drop(p_drop, seed, offset);
   if (attn::bwd_dsum(a, true) != hipSuccess) return ATTN_E_HIP;
   if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
   if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;

@@ -94,7 +94,7 @@ __device__ __forceinline__ void pipeline_reads2() {
 template <int N>
 using int_c = std::integral_constant<int, N>;
 
-template <int D, bool CAUSAL, bool SPARSE, bool QK>
+template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP>
 __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ K,
                                                         const uint16_t* __restrict__ V,
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
                                                         uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                                                         int n, int nkb, int total, float scale, float sl2e,
                                                         const uint8_t* __restrict__ bmask, long long mask_stride,
-                                                        int nk_arg, int coff_arg) {
+                                                        int nk_arg, int coff_arg, DropArgs dr) {
   constexpr int NW = 8, BKV = 128, BQ = 64;
   constexpr int TB = BQ * D * 2;  // bytes per 64-row tile
   constexpr int IPW = (D / 8) / NW;  // DMA loads per wave per tile
@@ -206,8 +206,9 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   auto dma = [&](int i, auto b) ATTN_INLINE {
     if (w == 0) {
       const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)i * (BQ * 4));
-      dma_row64_asm(rl, lse_at(b), off, lane);
-      dma_row64_asm(rd, dsm_at(b), off, lane);
+      const uint32_t sbase = (uint32_t)(uintptr_t)(ATTN_LDS char*)smem;
+      dma_row64_asm(rl, sbase + 512u * decltype(b)::value, off, lane);
+      dma_row64_asm(rd, sbase + 512u * decltype(b)::value + 256u, off, lane);
     }
     dma_tile_asm<D, NW>(rq, q_at(b), i * BQ, w, lane);
     dma_tile_asm<D, NW>(rdo, g_at(b), i * BQ, w, lane);
@@ -232,6 +233,47 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   };
 
   float* px = pxs + grp * (2 * 4 * 64 * 4);
+
+  // Dropout keep bits of this lane's key for queries qbase + 0..3 (bit k).
+  // One generator call covers four consecutive keys of one query, so the
+  // four lanes of a quad (keys 4a .. 4a + 3) call it for the four queries
+  // and exchange words by a 4 x 4 transpose within the quad (DPP rotations).
+  auto quad_keep = [&](int qbase) ATTN_INLINE -> uint32_t {
+    const int tq = lane & 3;
+    const u32x4 wd = philox4x32_10((uint32_t)(kw0 + (l32 & ~3)) >> 2, (uint32_t)(qbase + tq), (uint32_t)bh,
+                                   dr.offset, dr.seed_lo, dr.seed_hi);
+    // y[k] = word tq of quad lane k: query qbase + k, this lane's key.
+    uint32_t y[4];
+    auto pick = [&](int idx) ATTN_INLINE {
+      return idx == 0 ? wd[0] : idx == 1 ? wd[1] : idx == 2 ? wd[2] : wd[3];
+    };
+#pragma unroll
+    for (int k = 0; k < 4; ++k) y[k] = 0u;
+    y[0] = tq == 0 ? wd[0] : y[0];
+    y[1] = tq == 1 ? wd[1] : y[1];
+    y[2] = tq == 2 ? wd[2] : y[2];
+    y[3] = tq == 3 ? wd[3] : y[3];
+    auto rot = [&](auto rc) ATTN_INLINE {
+      constexpr int RT = decltype(rc)::value;
+      // Lane s sends its word (s - RT) mod 4; lane r receives from lane
+      // (r + RT) mod 4 its word r.
+      const uint32_t x = pick((tq - RT) & 3);
+      constexpr int ctrl = ((0 + RT) & 3) | (((1 + RT) & 3) << 2) | (((2 + RT) & 3) << 4) | (((3 + RT) & 3) << 6);
+      const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, 0xF, 0xF, false);
+      const int src = (tq + RT) & 3;
+      y[0] = src == 0 ? r : y[0];
+      y[1] = src == 1 ? r : y[1];
+      y[2] = src == 2 ? r : y[2];
+      y[3] = src == 3 ? r : y[3];
+    };
+    rot(int_c<1>{});
+    rot(int_c<2>{});
+    rot(int_c<3>{});
+    uint32_t bits = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bits |= (y[k] >= dr.thr ? 1u : 0u) << k;
+    return bits;
+  };
 
   // Products of P or dS for one half tile into dV or dK.  Where the half
   // tile holds a magnitude >= 1/16 the values enter as hi + lo bf16 pairs (a
@@ -359,16 +401,27 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * t + 8 * g + 4 * hh]);
+            const int qbase = i * BQ + 32 * t + 8 * g + 4 * hh;  // queries qbase + k of registers 4g + k
+            uint32_t keep = 0xFu;
+            if constexpr (DROP) keep = quad_keep(qbase);
             f32x4 o;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               float pv = fast_exp2(fmaf(t == 0 ? c0[4 * g + k] : c1[4 * g + k], sl2e, -l4[k]));
               if (need_mask) {
-                const int q = i * BQ + 32 * t + 8 * g + 4 * hh + k;
+                const int q = qbase + k;
                 pv = key > q + coff ? 0.f : pv;
               }
-              v[t][4 * g + k] = pv;
-              o[k] = pv;
+              if constexpr (DROP) {
+                // dV takes the dropped, rescaled probability; the dP wave
+                // gets P with the keep bit in the sign (P >= 0).
+                const bool kept = (keep >> k) & 1u;
+                v[t][4 * g + k] = kept ? pv * dr.keep_scale : 0.f;
+                o[k] = kept ? pv : -pv;
+              } else {
+                v[t][4 * g + k] = pv;
+                o[k] = pv;
+              }
             }
             *reinterpret_cast<f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]) = o;
           }
@@ -418,8 +471,9 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
           const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dsms[32 + 8 * g + 4 * hh]);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            c0[4 * g + k] = -d0[k];
-            c1[4 * g + k] = -d1[k];
+            // With dropout dP is needed alone (dS = P (Z dP / (1 - p) - D)).
+            c0[4 * g + k] = DROP ? 0.f : -d0[k];
+            c1[4 * g + k] = DROP ? 0.f : -d1[k];
           }
         }
         chains(TR, g_at(b), c0, c1);
@@ -433,8 +487,18 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x4 p4 = *reinterpret_cast<const f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]);
+            if constexpr (DROP) {
+              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsm_at(b)[32 * t + 8 * g + 4 * hh]);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[4 * g + k] = (t == 0 ? c0[4 * g + k] : c1[4 * g + k]) * p4[k];
+              for (int k = 0; k < 4; ++k) {
+                const float dpv = t == 0 ? c0[4 * g + k] : c1[4 * g + k];
+                const bool kept = (__float_as_uint(p4[k]) >> 31) == 0u;
+                v[4 * g + k] = fabsf(p4[k]) * ((kept ? dpv * dr.keep_scale : 0.f) - d4[k]);
+              }
+            } else {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) v[4 * g + k] = (t == 0 ? c0[4 * g + k] : c1[4 * g + k]) * p4[k];
+            }
           }
           const bool sp = needs_split(v);
           (t == 0 ? spl0 : spl1) = sp;
@@ -472,7 +536,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // dQ: query-stationary
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __restrict__ Q,
                                                            const uint16_t* __restrict__ K,
                                                            const uint16_t* __restrict__ V,
@@ -482,7 +546,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
                                                            uint16_t* __restrict__ dQ, int n, int nqb, int total,
                                                            float scale, float sl2e,
                                                            const uint8_t* __restrict__ bmask, long long mask_stride,
-                                                           int nb, int nk_arg, int coff_arg) {
+                                                           int nb, int nk_arg, int coff_arg, DropArgs dr) {
   constexpr int BR = NW * 32, BC = 64;
 
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[BC * D];
@@ -542,6 +606,18 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
       // One half tile at a time: interleaving the halves costs more
       // registers than the file holds at two waves per SIMD.
       __builtin_amdgcn_sched_barrier(0);
+      // Dropout: bit r kept (keys j0 + 32t + 8g + 4hh + 0..3 are one call).
+      uint32_t keep = 0xFFFFu;
+      if constexpr (DROP) {
+        keep = 0u;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x4 wd = philox4x32_10((uint32_t)(j0 + 32 * t + 8 * g + 4 * hh) >> 2, (uint32_t)qrow, (uint32_t)bh,
+                                         dr.offset, dr.seed_lo, dr.seed_hi);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) keep |= (wd[i] >= dr.thr ? 1u : 0u) << (4 * g + i);
+        }
+      }
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -554,9 +630,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
         pacc = mfma32(TR.rows(vs, 32 * t, s), gf[s], pacc);
       }
 
+      auto dp_of = [&](int r) ATTN_INLINE {
+        if constexpr (DROP)
+          return (keep >> r) & 1u ? pacc[r] * dr.keep_scale : 0.f;
+        else
+          return pacc[r];
+      };
       float ds[16];
-      if constexpr (CAUSAL) {
-        // Exponent arguments; entries above the diagonal (diagonal tiles
+      if constexpr (CAUSAL || DROP) {
+        // Exponent arguments; masked entries (diagonal and ragged tiles
         // only, a wave-uniform branch) become -inf, whose exp2 is 0.  Keys
         // past n lie above the diagonal of every row that is written.
         float x[16];
@@ -566,11 +648,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kj = j0 + 32 * t + crow(r, hh);
-            x[r] = kj > qrow + coff ? -INFINITY : x[r];
+            x[r] = (CAUSAL ? kj > qrow + coff : kj >= nk) ? -INFINITY : x[r];
           }
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(x[r]) * (pacc[r] - dq_d);
+        for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(x[r]) * (dp_of(r) - dq_d);
       } else {
         // Full mask: only keys past n (ragged last tile) are masked; the
         // compiler turns this into selects, which keeps the loop within the
@@ -579,7 +661,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
         for (int r = 0; r < 16; ++r) {
           float pv = fast_exp2(fmaf(sacc[r], sl2e, -l2));
           if (need_mask) pv = (j0 + 32 * t + crow(r, hh) >= nk) ? 0.f : pv;
-          ds[r] = pv * (pacc[r] - dq_d);
+          ds[r] = pv * (dp_of(r) - dq_d);
         }
       }
 #pragma unroll
@@ -691,16 +773,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE, bool QK>
+template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false>
 hipError_t launch_dkdv(const BwdArgs& a) {
   const int n = (int)a.n;
   const int nk = QK ? (int)a.nk : n;
   const int nkb = (nk + 127) / 128;
   const int total = (int)(a.bh * nkb);
-  hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, SPARSE, QK>), dim3(total), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, SPARSE, QK, DROP>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e,
-                     a.bmask, (long long)a.mask_stride, nk, nk - n);
+                     a.bmask, (long long)a.mask_stride, nk, nk - n, a.drop);
   return hipGetLastError();
 }
 
@@ -708,7 +790,7 @@ hipError_t launch_dkdv(const BwdArgs& a) {
 #define ATTN_DQ_NW128 8  // waves per dQ workgroup at d = 128 (tuning knob)
 #endif
 
-template <int D, bool CAUSAL, bool SPARSE, bool QK>
+template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false>
 hipError_t launch_dq(const BwdArgs& a) {
   // Block-sparse: one mask block row per workgroup (4 waves), so that every
   // wave of a workgroup wants every tile the workgroup fetches.
@@ -718,10 +800,10 @@ hipError_t launch_dq(const BwdArgs& a) {
   const int total = (int)(a.bh * nqb);
   const int nb = (n + kSparseBlock - 1) / kSparseBlock;
   const int nk = QK ? (int)a.nk : n;
-  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK>), dim3(total), dim3(NW * 64), 0, a.stream,
+  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK, DROP>), dim3(total), dim3(NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.dsum, (uint16_t*)a.dq, n, nqb, total, a.scale, a.scale * kLog2e, a.bmask,
-                     (long long)a.mask_stride, nb, nk, nk - n);
+                     (long long)a.mask_stride, nb, nk, nk - n, a.drop);
   return hipGetLastError();
 }
 
@@ -740,12 +822,20 @@ hipError_t dq_t(const BwdArgs& a) {
 }  // namespace
 
 hipError_t bwd_bf16_dkdv(const BwdArgs& a) {
+  if (a.dropout) {  // dense, square lengths only (checked by the caller)
+    if (a.d == 64) return a.causal ? launch_dkdv<64, true, false, false, true>(a) : launch_dkdv<64, false, false, false, true>(a);
+    return a.causal ? launch_dkdv<128, true, false, false, true>(a) : launch_dkdv<128, false, false, false, true>(a);
+  }
   if (a.bmask) return dkdv_t<true, false>(a);
   if (a.nk >= 0) return dkdv_t<false, true>(a);
   return dkdv_t<false, false>(a);
 }
 
 hipError_t bwd_bf16_dq(const BwdArgs& a) {
+  if (a.dropout) {
+    if (a.d == 64) return a.causal ? launch_dq<64, true, false, false, true>(a) : launch_dq<64, false, false, false, true>(a);
+    return a.causal ? launch_dq<128, true, false, false, true>(a) : launch_dq<128, false, false, false, true>(a);
+  }
   if (a.bmask) return dq_t<true, false>(a);
   if (a.nk >= 0) return dq_t<false, true>(a);
   return dq_t<false, false>(a);

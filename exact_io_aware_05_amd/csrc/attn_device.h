@@ -136,6 +136,38 @@ __device__ __forceinline__ u32x4 load16_or_zero(const uint16_t* p, bool ok) {
   return ok ? *reinterpret_cast<const u32x4*>(p) : z;
 }
 
+// Philox4x32 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel random
+// numbers: as easy as 1, 2, 3", SC 2011): counter (c0, c1, c2, c3), key
+// (k0, k1); each round takes the full 64-bit products c0 * 0xD2511F53 and
+// c2 * 0xCD9E8D57 and sets (c0, c1, c2, c3) to (hi(c2 M1) ^ c1 ^ k0,
+// lo(c2 M1), hi(c0 M0) ^ c3 ^ k1, lo(c0 M0)); the key gains (0x9E3779B9,
+// 0xBB67AE85) before every round but the first.  The key is wave-uniform
+// here, so its schedule is scalar work.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                               uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+    const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  u32x4 w;
+  w[0] = c0;
+  w[1] = c1;
+  w[2] = c2;
+  w[3] = c3;
+  return w;
+}
+
 // Workgroup order.  Workgroups are handed to the 8 XCDs of the chip round
 // robin (id % 8).  This maps the hardware id to a logical id so that each
 // XCD receives a contiguous range of logical ids (tiles of the same head

@@ -45,7 +45,7 @@
 
 namespace attn {
 
-template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
                                                                    const uint16_t* __restrict__ K,
                                                                    const uint16_t* __restrict__ V,
@@ -53,7 +53,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
                                                                    float* __restrict__ LSE, int n, int nqb,
                                                                    int total, float c, uint32_t qsign,
                                                                    const uint8_t* __restrict__ bmask,
-                                                                   long long mask_stride, int nb, QkKernelArgs qa) {
+                                                                   long long mask_stride, int nb, QkKernelArgs qa,
+                                                                   DropArgs dr) {
   constexpr int BC = 64;               // keys per K/V tile
   constexpr int BU = 32;               // keys per pipeline unit (half a tile)
   constexpr int BR = NW * 32;          // query rows per workgroup
@@ -205,8 +206,37 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   // a unit that must not contribute is masked to -inf (probabilities 0, so
   // its output products add zeros to finite V rows), and the matrix and
   // vector work can be interleaved freely.
+  // Dropout: keep bit r of a unit starting at key j0 for this lane's query;
+  // the four words of one generator call cover keys j0 + 8g + 4hh + 0..3,
+  // which are exactly registers 4g .. 4g + 3.
+  auto keep_bits = [&](int j0) ATTN_INLINE -> uint32_t {
+    uint32_t bits = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x4 wd = philox4x32_10((uint32_t)(j0 + 8 * g + 4 * hh) >> 2, (uint32_t)qrow, (uint32_t)bh, dr.offset,
+                                     dr.seed_lo, dr.seed_hi);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bits |= (wd[i] >= dr.thr ? 1u : 0u) << (4 * g + i);
+    }
+    return bits;
+  };
+  // Probabilities as they enter the output products: dropped ones are 0,
+  // kept ones scaled by 1 / (1 - p) (the row sum keeps all of them).
+  auto pack_p = [&](const float* p, uint32_t keep, bf16x8(&pn)[2]) ATTN_INLINE {
+    if constexpr (DROP) {
+      float pd[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pd[r] = (keep >> r) & 1u ? p[r] * dr.keep_scale : 0.f;
+      pn[0] = pack_bf16x8(pd);
+      pn[1] = pack_bf16x8(pd + 8);
+    } else {
+      pn[0] = pack_bf16x8(p);
+      pn[1] = pack_bf16x8(p + 8);
+    }
+  };
+
   auto step = [&](auto has_pv, f32x16& sc, f32x16& sn, bf16x8(&pn)[2], const bf16x8(&po)[2], const uint16_t* kb,
-                  const uint16_t* vb) ATTN_INLINE -> float {
+                  const uint16_t* vb, int j0, uint32_t& keep) ATTN_INLINE -> float {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sn[r] = 0.f;
 #pragma unroll
@@ -224,15 +254,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
       p[r] = fast_exp2(fmaf(sc[r], c, -mc));
       a[r & 3] = r < 4 ? p[r] : a[r & 3] + p[r];
     }
-    pn[0] = pack_bf16x8(p);
-    pn[1] = pack_bf16x8(p + 8);
+    if constexpr (DROP) keep = keep_bits(j0);
+    pack_p(p, keep, pn);
     // Keep the conversions here, so the 16 probabilities die in this step.
     asm volatile("" ::"v"(pn[0]), "v"(pn[1]));
     // Interleave: each matrix product is preceded by LDS reads for a later
     // one and followed by a share of the exponential work (masks: 0x100 LDS
     // read, 0x008 MFMA, 0x402 VALU).
     constexpr int NP = D / 16;
-    constexpr int VPM = (56 + 2 * NP - 1) / (2 * NP);
+    constexpr int NV = DROP ? 56 + 200 : 56;  // vector instructions per step, about
+    constexpr int VPM = (NV + 2 * NP - 1) / (2 * NP);
     __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -247,7 +278,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
 
   // After a step: if some lane's unit sum exceeds the gate, raise the
   // reference to the unit's max, rescale, and recompute the unit.
-  auto settle = [&](f32x16& sc, bf16x8(&pn)[2], float ps) ATTN_INLINE {
+  auto settle = [&](f32x16& sc, bf16x8(&pn)[2], float ps, uint32_t keep) ATTN_INLINE {
     if (__builtin_amdgcn_ballot_w64(ps > gate) != 0) {
       float mx = -INFINITY;
 #pragma unroll
@@ -270,8 +301,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
         p[r] = fast_exp2(fmaf(sc[r], c, -mc));
         ps += p[r];
       }
-      pn[0] = pack_bf16x8(p);
-      pn[1] = pack_bf16x8(p + 8);
+      pack_p(p, keep, pn);
     }
     lsum += ps;
   };
@@ -298,8 +328,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
           sc[r] = dead ? -INFINITY : sc[r];
         }
       }
-      const float ps = step(std::bool_constant<(k > 0)>{}, sc, sn, pn, po, kb, vb);
-      settle(sc, pn, ps);
+      uint32_t keep = 0xFFFFu;
+      const float ps = step(std::bool_constant<(k > 0)>{}, sc, sn, pn, po, kb, vb, j0, keep);
+      settle(sc, pn, ps, keep);
     };
     if constexpr (ODD)
       go(s1, s0, p1, p0);
@@ -392,7 +423,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   }
 }
 
-template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false>
 static hipError_t launch_fwd(const FwdArgs& a) {
   constexpr int BR = NW * 32;
   const int nqb = (int)((a.n + BR - 1) / BR);
@@ -414,9 +445,9 @@ static hipError_t launch_fwd(const FwdArgs& a) {
     qa.opart = a.opart;
     qa.lpart = a.lpart;
   }
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK>), dim3(total), dim3(NW * 64), 0, a.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK, DROP>), dim3(total), dim3(NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb, qa);
+                     (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb, qa, a.drop);
   return hipGetLastError();
 }
 
@@ -428,6 +459,12 @@ static hipError_t fwd_bf16_t(const FwdArgs& a) {
 }
 
 hipError_t fwd_bf16(const FwdArgs& a) {
+  if (a.dropout) {
+    // Dense, square lengths only (checked by the caller).
+    if (a.d == 64)
+      return a.causal ? launch_fwd<64, 4, true, false, false, true>(a) : launch_fwd<64, 4, false, false, false, true>(a);
+    return a.causal ? launch_fwd<128, 4, true, false, false, true>(a) : launch_fwd<128, 4, false, false, false, true>(a);
+  }
   if (a.bmask) return fwd_bf16_t<true, false>(a);
   if (a.nk >= 0) return fwd_bf16_t<false, true>(a);
   return fwd_bf16_t<false, false>(a);

@@ -8,6 +8,17 @@
 
 namespace attn {
 
+// Dropout on the probabilities (bf16, square lengths, dense): the element
+// (query i, key j) of head bh is kept when word j % 4 of
+// Philox4x32-10(counter (j / 4, i, bh, offset), key (seed_lo, seed_hi)) is
+// >= thr; kept probabilities are multiplied by keep_scale = 1 / (1 - p).
+struct DropArgs {
+  uint32_t thr = 0;
+  float keep_scale = 1.f;
+  uint32_t seed_lo = 0, seed_hi = 0;
+  uint32_t offset = 0;
+};
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -35,6 +46,8 @@ struct FwdArgs {
   int kchunk = 0;
   float* opart = nullptr;
   float* lpart = nullptr;
+  bool dropout = false;  // with `drop`
+  DropArgs drop;
 };
 
 // Kernel-side view of the unequal-length arguments.
@@ -67,6 +80,8 @@ struct BwdArgs {
   const uint8_t* bmask = nullptr;  // as in FwdArgs
   int64_t mask_stride = 0;
   int64_t nk = -1;  // as in FwdArgs (no split in the backward)
+  bool dropout = false;
+  DropArgs drop;
 };
 
 // Block size of the block-sparse mask (query and key rows per block).

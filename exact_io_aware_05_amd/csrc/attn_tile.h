@@ -128,25 +128,32 @@ __device__ __forceinline__ void dma_tile_asm(const RsrcWords& rs, uint16_t* lds,
     const int k = w * IPW + r;
     const uint32_t xk = D == 128 ? 16u * (k & 3) : 32u * (k & 1);
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(l0 + 1024u * k);
+    uint32_t saved;
     asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "buffer_load_dwordx4 %1, %2, 0 offen lds"
-        :
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
         : "s"(m0), "v"(base + 1024u * k + (b ^ xk)), "s"(rs.w)
-        : "memory", "m0");
+        : "memory");
   }
 }
 
 // 64 consecutive fp32 values (one per lane: bytes 4 * lane) into LDS at
-// `lds`, through the same invisible path.
-__device__ __forceinline__ void dma_row64_asm(const RsrcWords& rs, float* lds, uint32_t byte_off, int lane) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(ATTN_LDS float*)lds);
+// byte address `lds_addr`, through the same invisible path.  (M0, which
+// addresses the LDS side of these loads, is restored after each one.)
+__device__ __forceinline__ void dma_row64_asm(const RsrcWords& rs, uint32_t lds_addr, uint32_t byte_off, int lane) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  uint32_t saved;
   asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "buffer_load_dword %1, %2, 0 offen lds"
-      :
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
       : "s"(m0), "v"(byte_off + 4u * (uint32_t)lane), "s"(rs.w)
-      : "memory", "m0");
+      : "memory");
 }
 
 // Per-lane LDS byte offsets for reading MFMA operand fragments from tiles in

@@ -63,7 +63,8 @@ typedef enum {
   ATTN_E_UNSUPPORTED = -3, /* head dimension or dtype not supported */
   ATTN_E_SCALE = -4,       /* scale is NaN or infinite */
   ATTN_E_WORKSPACE = -5,   /* workspace missing or smaller than required */
-  ATTN_E_HIP = -6          /* a HIP launch failed */
+  ATTN_E_HIP = -6,         /* a HIP launch failed */
+  ATTN_E_DROPOUT = -7      /* dropout probability outside [0, 1) or NaN */
 } attn_status;
 
 /*
@@ -232,6 +233,45 @@ int attn_bwd_qk(const void* q, const void* k, const void* v, const void* o,
                 void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
                 int64_t d, int dtype, int causal, float scale, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/*
+ * Dropout on the probabilities.  The pages list dropout among the
+ * element-wise operations kernel fusion folds into one kernel ("Background",
+ * Paper Notes) and fix no formula; this is the usual attention dropout:
+ *
+ *   O = (P * Z) V / (1 - p_drop),  LSE as without dropout (the statistics of
+ *   S; the backward pass recomputes P from it),
+ *
+ * with Z_ij in {0, 1}.  Z is drawn by Philox4x32-10 (Salmon, Moraes, Dror,
+ * Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), nothing is
+ * stored: for head bh = b * H + h, query i and key j, the counter is
+ * (j / 4, i, bh, offset mod 2^32) and the key (seed mod 2^32, seed / 2^32);
+ * output word j % 4 is compared with t = min(floor(p_drop * 2^32), 2^32 - 1)
+ * and the element is kept when the word is >= t (p_drop = 0 keeps every
+ * element and gives attn_fwd's results bit for bit).  The backward pass
+ * regenerates the same Z, so attn_bwd_dropout must get the p_drop, seed and
+ * offset (and causal, scale) of the forward:
+ *
+ *   dV = (P * Z)^T dO / (1 - p),  dP = (dO V^T) * Z / (1 - p),
+ *   dS = P * (dP - D) with D_i = sum_k dO_ik O_ik,  dQ = scale dS K,
+ *   dK = scale dS^T Q.
+ *
+ * bf16 only (ATTN_FP32 returns ATTN_E_UNSUPPORTED); p_drop outside [0, 1)
+ * or NaN returns ATTN_E_DROPOUT.  The backward workspace is that of attn_bwd
+ * (attn_bwd_workspace_bytes).  Other arguments, ownership and errors as for
+ * attn_fwd / attn_bwd.  Deterministic for given inputs, seed and offset.
+ */
+int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o,
+                     float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                     int dtype, int causal, float scale, float p_drop,
+                     uint64_t seed, uint64_t offset, void* stream);
+
+int attn_bwd_dropout(const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int dtype, int causal, float scale,
+                     float p_drop, uint64_t seed, uint64_t offset,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -31,12 +31,14 @@ def test_header_declares_the_boundary():
         "attn_bwd_blocksparse",
         "attn_bwd_dkdv",
         "attn_bwd_dq",
+        "attn_bwd_dropout",
         "attn_bwd_dsum",
         "attn_bwd_qk",
         "attn_bwd_qk_workspace_bytes",
         "attn_bwd_workspace_bytes",
         "attn_fwd",
         "attn_fwd_blocksparse",
+        "attn_fwd_dropout",
         "attn_fwd_qk",
         "attn_fwd_qk_workspace_bytes",
         "attn_status_string",
@@ -211,3 +213,19 @@ def test_product_path_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text, os.path.join(dirpath, f)
+
+
+def test_dropout_arguments_are_validated_before_any_launch():
+    E, L = _lib()
+    f = [FAKE] * 5
+    assert L.attn_fwd_dropout(None, *f[1:], 1, 1, 16, 64, 0, 0, 0.1, 0.1, 1, 0, None) == -1
+    assert L.attn_fwd_dropout(*f, 1, 1, 16, 64, 1, 0, 0.1, 0.1, 1, 0, None) == -3  # fp32: unsupported
+    assert L.attn_fwd_dropout(*f, 1, 1, 16, 48, 0, 0, 0.1, 0.1, 1, 0, None) == -3
+    assert L.attn_fwd_dropout(*f, 1, 1, 16, 64, 0, 0, float("inf"), 0.1, 1, 0, None) == -4
+    for p in (-0.1, 1.0, 1.5, float("nan")):
+        assert L.attn_fwd_dropout(*f, 1, 1, 16, 64, 0, 0, 0.1, p, 1, 0, None) == -7
+    g = [FAKE] * 9
+    assert L.attn_bwd_dropout(*g, 1, 1, 16, 64, 0, 0, 0.1, 1.0, 1, 0, FAKE, 1 << 20, None) == -7
+    assert L.attn_bwd_dropout(*g, 1, 1, 16, 64, 0, 0, 0.1, 0.2, 1, 0, None, 1 << 20, None) == -5
+    assert L.attn_bwd_dropout(*g, 1, 1, 16, 64, 0, 0, 0.1, 0.2, 1, 0, FAKE, 16, None) == -5
+    assert E.attn_status_string(-7).startswith("dropout probability")
