@@ -15,6 +15,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
                                           per block density and mask)
        python bench.py --decode          (unequal lengths: split-K/V decoding
                                           and chunked prefill, one JSON line each)
+       python bench.py --dropout         (fused dropout against the plain path,
+                                          one JSON line per mask)
        python bench.py --profile-pass    (one step plus a plain copy of known
                                           size, for hardware-counter runs)
 
@@ -243,6 +245,7 @@ def main():
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--blocksparse", action="store_true")
     ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--dropout", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -284,6 +287,10 @@ def main():
 
     if args.decode:
         decode(torch, E, args.steps, args.warmup)
+        return
+
+    if args.dropout:
+        dropout(torch, E, args.steps, args.warmup)
         return
 
     shape = (4, 16, 4096, 128)
@@ -473,6 +480,36 @@ def _time_ms(torch, fn, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def dropout(torch, E, steps, warmup):
+    """Fused dropout against the plain path at B=4 H=16 N=4096 d=128, bf16:
+    forward and whole backward (D, dK/dV, dQ) per mask, p = 0.1, TFLOP/s by
+    the usual convention (the generator's work is not counted)."""
+    shape = (4, 16, 4096, 128)
+    b, h, n, d = shape
+    g = torch.Generator(device="cuda").manual_seed(17)
+    q, k, v, do = (torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16) for _ in range(4))
+    ws = torch.empty(max(E.attn_bwd_workspace_bytes(b, h, n, d, E.ATTN_BF16), 256), dtype=torch.uint8, device="cuda")
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    for causal in (False, True):
+        f = fwd_flops(b * h, n, d, causal)
+        o, lse = E.attn_fwd(q, k, v, causal=causal)
+        t_fwd = _time_ms(torch, lambda: E.attn_fwd(q, k, v, causal=causal, out=o, lse=lse), steps, warmup)
+        t_bwd = _time_ms(torch, lambda: E.attn_bwd(q, k, v, o, do, lse, causal=causal, workspace=ws, grads=grads),
+                         steps, warmup)
+        od, lsed = E.attn_fwd_dropout(q, k, v, 0.1, 1234, 0, causal=causal)
+        t_fwd_d = _time_ms(torch, lambda: E.attn_fwd_dropout(q, k, v, 0.1, 1234, 0, causal=causal, out=od, lse=lsed),
+                           steps, warmup)
+        t_bwd_d = _time_ms(torch, lambda: E.attn_bwd_dropout(q, k, v, od, do, lsed, 0.1, 1234, 0, causal=causal,
+                                                             workspace=ws, grads=grads), steps, warmup)
+        print(json.dumps({
+            "mode": "dropout", "mask": "causal" if causal else "full", "B": b, "H": h, "N": n, "d": d, "p": 0.1,
+            "fwd_ms": round(t_fwd_d, 4), "fwd_tflops": round(f / t_fwd_d / 1e9, 1),
+            "bwd_ms": round(t_bwd_d, 4), "bwd_tflops": round(2.5 * f / t_bwd_d / 1e9, 1),
+            "plain_fwd_ms": round(t_fwd, 4), "plain_bwd_ms": round(t_bwd, 4),
+            "fwd_cost": round(t_fwd_d / t_fwd, 3), "bwd_cost": round(t_bwd_d / t_bwd, 3),
+        }), flush=True)
 
 
 def decode(torch, E, steps, warmup):
