@@ -59,8 +59,8 @@ namespace {
 // i + 2 is issued once the mid-tile barrier of tile i has retired the reads
 // of tile i - 1.
 // ---------------------------------------------------------------------------
-// Magnitude from which P and dS enter the dV and dK products as hi + lo bf16
-// pairs (see bwd_kv_kernel).
+// Magnitude of a product term's weight from which P (in dV) and scale * dS
+// (in dK) enter the products as hi + lo bf16 pairs (see bwd_kv_kernel).
 constexpr float kSplitThreshold = 1.0f / 16.0f;
 
 // Schedule hint for a block of M operand reads feeding M MFMAs: issue half of
@@ -276,7 +276,8 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   };
 
   // Products of P or dS for one half tile into dV or dK.  Where the half
-  // tile holds a magnitude >= 1/16 the values enter as hi + lo bf16 pairs (a
+  // tile holds a weight (P, or scale * dS) >= 1/16 the values enter as hi +
+  // lo bf16 pairs (a
   // single bf16 rounding, relative 2^-9, of a probability near 1 can move a
   // column sum of magnitude > 4 by more than the output's own rounding
   // leaves); each term is one call, with packed operands h[u].
@@ -294,12 +295,16 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     pipeline_reads2<D / 16>();
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Wave-uniform test for the split.
+  // Wave-uniform test for the split.  P enters dV as it is; dS enters dK
+  // unscaled (the scale is applied to the accumulator at the end), so its
+  // threshold is divided by |scale|: a term's rounding error in the output
+  // is then bounded alike in both products.
+  const float tau = s_role ? kSplitThreshold : kSplitThreshold / fabsf(scale);
   auto needs_split = [&](const float* vt) ATTN_INLINE {
     float vmax = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, fabsf(vt[r]));
-    return __builtin_amdgcn_ballot_w64(vmax >= kSplitThreshold) != 0;
+    return __builtin_amdgcn_ballot_w64(vmax >= tau) != 0;
   };
   // Two independent MFMA chains (queries 0-31 and 32-63 of the tile) over
   // the row-major tile `src`, with this wave's key-side fragments.

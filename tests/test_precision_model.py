@@ -47,13 +47,14 @@ def test_single_bf16_probabilities_exceed_tolerance_and_hilo_does_not():
     assert err_hilo < 1.5e-2
 
 
-def _selective(p, tau=1.0 / 16, tq=32, tk=32):
-    """hi + lo only on 32 x 32 tiles holding a value >= tau, as the kernel does."""
+def _selective(p, tau=1.0 / 16, tq=32, tk=32, weight=1.0):
+    """hi + lo only on 32 x 32 tiles holding a value with weight * |value| >=
+    tau, as the kernel does."""
     out = _bf16(p)
     full = _hilo(p)
     for i in range(0, p.shape[0], tq):
         for j in range(0, p.shape[1], tk):
-            if np.abs(p[i : i + tq, j : j + tk]).max() >= tau:
+            if weight * np.abs(p[i : i + tq, j : j + tk]).max() >= tau:
                 out[i : i + tq, j : j + tk] = full[i : i + tq, j : j + tk]
     return out
 
@@ -75,3 +76,29 @@ def test_selective_split_keeps_the_full_split_accuracy():
             err_sel = max(err_sel, np.abs(_bf16(_selective(p).T @ do[b, h]) - ref).max())
             err_hilo = max(err_hilo, np.abs(_bf16(_hilo(p).T @ do[b, h]) - ref).max())
     assert err_sel <= err_hilo + 1e-4
+
+
+def test_selective_split_of_scaled_ds_keeps_the_full_split_accuracy():
+    """dS enters dK unscaled and the scale multiplies the sum, so the kernel
+    compares scale * |dS| with 1/16: a term's rounding error in dK is then
+    bounded as a term's in dV.  That selects few tiles at long N and keeps the
+    worst dK error at that of splitting every tile."""
+    for shape, causal in (((2, 2, 129, 128), True), ((1, 2, 1000, 128), False)):
+        seed = 2000 + sum(shape) + 11
+        inp = synth.qkvdo(seed, shape, "bf16")
+        scale = 1.0 / math.sqrt(shape[3])
+        q, k, v, do = inp["q"], inp["k"], inp["v"], inp["do"]
+        o, lse = A.forward(q, k, v, causal, scale)
+        _, dk_ref, _ = A.backward(q, k, v, do, causal, scale)
+        err_sel, err_hilo = 0.0, 0.0
+        for b in range(shape[0]):
+            for h in range(shape[1]):
+                p = np.exp(A.scores(q[b, h], k[b, h], scale, causal) - lse[b, h][:, None])
+                dsum = (do[b, h] * o[b, h]).sum(-1, keepdims=True)
+                ds = p * (do[b, h] @ v[b, h].T - dsum)
+                ref = dk_ref[b, h]
+                sel = _selective(ds, weight=scale)
+                err_sel = max(err_sel, np.abs(_bf16(scale * (sel.T @ q[b, h])) - ref).max())
+                err_hilo = max(err_hilo, np.abs(_bf16(scale * (_hilo(ds).T @ q[b, h])) - ref).max())
+        assert err_sel <= err_hilo + 2e-4, (shape, err_sel, err_hilo)
+        assert err_sel < 1e-2
