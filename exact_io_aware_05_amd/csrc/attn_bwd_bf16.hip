@@ -602,7 +602,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   const int kend = CAUSAL ? min(nk, q0 + BR + coff) : nk;
   const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
 
-  auto compute = [&](const uint16_t* ks, const uint16_t* vs, int j0) {
+  // TAIL: the tile may hold keys past nk (only the last tile can); the full
+  // mask path masks them only in such calls.
+  auto compute = [&](const uint16_t* ks, const uint16_t* vs, int j0, auto tail) ATTN_INLINE {
+    constexpr bool TAIL = decltype(tail)::value;
     const bool active = !CAUSAL || (j0 <= wq0 + 31 + coff);
     if (!active) return;
     const bool need_mask = (j0 + BC > nk) || (CAUSAL && j0 + BC - 1 > wq0 + coff);
@@ -623,11 +626,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
           for (int i = 0; i < 4; ++i) keep |= (wd[i] >= dr.thr ? 1u : 0u) << (4 * g + i);
         }
       }
+      // dP accumulates onto -D (it ends as dP - D), except with dropout,
+      // where dP itself is needed (dS = P (Z dP / (1 - p) - D)).
       f32x16 sacc, pacc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sacc[r] = 0.f;
-        pacc[r] = 0.f;
+        pacc[r] = DROP ? 0.f : -dq_d;
       }
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
@@ -635,9 +640,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
         pacc = mfma32(TR.rows(vs, 32 * t, s), gf[s], pacc);
       }
 
-      auto dp_of = [&](int r) ATTN_INLINE {
+      // dP - D of register r.
+      auto dpd_of = [&](int r) ATTN_INLINE {
         if constexpr (DROP)
-          return (keep >> r) & 1u ? pacc[r] * dr.keep_scale : 0.f;
+          return ((keep >> r) & 1u ? pacc[r] * dr.keep_scale : 0.f) - dq_d;
         else
           return pacc[r];
       };
@@ -657,16 +663,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
           }
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(x[r]) * (dp_of(r) - dq_d);
+        for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(x[r]) * dpd_of(r);
       } else {
-        // Full mask: only keys past n (ragged last tile) are masked; the
-        // compiler turns this into selects, which keeps the loop within the
-        // register file at two waves per SIMD.
+        // Full mask: only keys past nk (in the last tile) are masked, as
+        // selects, in the calls that may hold them.
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pv = fast_exp2(fmaf(sacc[r], sl2e, -l2));
-          if (need_mask) pv = (j0 + 32 * t + crow(r, hh) >= nk) ? 0.f : pv;
-          ds[r] = pv * (dp_of(r) - dq_d);
+          if (TAIL && need_mask) pv = (j0 + 32 * t + crow(r, hh) >= nk) ? 0.f : pv;
+          ds[r] = pv * dpd_of(r);
         }
       }
 #pragma unroll
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
     __syncthreads();
     auto tile = [&](int p) ATTN_INLINE { return __builtin_amdgcn_readfirstlane((int)tlist[p]); };
     auto run_tile = [&](const uint16_t* ks, const uint16_t* vs, int e) ATTN_INLINE {
-      if ((e >> qsub) & 1) compute(ks, vs, (e >> 2) * BC);
+      if ((e >> qsub) & 1) compute(ks, vs, (e >> 2) * BC, std::true_type{});
     };
     if (cnt > 0) {
       dma_tile<D, NW>(rk, k0s, (tile(0) >> 2) * BC, w, lane);
@@ -737,31 +742,66 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
       wait_vmem();
       __syncthreads();
     }
-  } else {
-  if (!QK || ntiles > 0) {
-    dma_tile<D, NW>(rk, k0s, 0, w, lane);
-    dma_tile<D, NW>(rv, v0s, 0, w, lane);
-    wait_vmem();
-    __syncthreads();
-  }
-
-  for (int jt = 0; jt < ntiles; jt += 2) {
-    if (jt + 1 < ntiles) {
-      dma_tile<D, NW>(rk, k1s, (jt + 1) * BC, w, lane);
-      dma_tile<D, NW>(rv, v1s, (jt + 1) * BC, w, lane);
+  } else if constexpr (CAUSAL) {
+    // Causal: every tile may need the diagonal mask (a branch inside
+    // compute), and two call sites keep the loop within the register file.
+    if (ntiles > 0) {
+      dma_tile<D, NW>(rk, k0s, 0, w, lane);
+      dma_tile<D, NW>(rv, v0s, 0, w, lane);
+      wait_vmem();
+      __syncthreads();
     }
-    compute(k0s, v0s, jt * BC);
-    wait_vmem();
-    __syncthreads();
-    if (jt + 1 >= ntiles) break;
-    if (jt + 2 < ntiles) {
-      dma_tile<D, NW>(rk, k0s, (jt + 2) * BC, w, lane);
-      dma_tile<D, NW>(rv, v0s, (jt + 2) * BC, w, lane);
+    for (int jt = 0; jt < ntiles; jt += 2) {
+      if (jt + 1 < ntiles) {
+        dma_tile<D, NW>(rk, k1s, (jt + 1) * BC, w, lane);
+        dma_tile<D, NW>(rv, v1s, (jt + 1) * BC, w, lane);
+      }
+      compute(k0s, v0s, jt * BC, std::true_type{});
+      wait_vmem();
+      __syncthreads();
+      if (jt + 1 >= ntiles) break;
+      if (jt + 2 < ntiles) {
+        dma_tile<D, NW>(rk, k0s, (jt + 2) * BC, w, lane);
+        dma_tile<D, NW>(rv, v0s, (jt + 2) * BC, w, lane);
+      }
+      compute(k1s, v1s, (jt + 1) * BC, std::true_type{});
+      wait_vmem();
+      __syncthreads();
     }
-    compute(k1s, v1s, (jt + 1) * BC);
-    wait_vmem();
-    __syncthreads();
-  }
+  } else if (ntiles > 0) {
+    // Tiles 0 .. last - 1 in pairs (buffer 0, buffer 1), each pair fetching
+    // the next two, with no exit inside the pair: a loop that could leave
+    // between its two halves made the register allocator copy the dQ
+    // accumulators on every tile.  The last tile (the only one that can
+    // hold keys past nk) follows the loop.
+    const int last = ntiles - 1;
+    auto fetch = [&](uint16_t* ks, uint16_t* vs, int jt) ATTN_INLINE {
+      dma_tile<D, NW>(rk, ks, jt * BC, w, lane);
+      dma_tile<D, NW>(rv, vs, jt * BC, w, lane);
+    };
+    auto settle = [&]() ATTN_INLINE {
+      wait_vmem();
+      __syncthreads();
+    };
+    fetch(k0s, v0s, 0);
+    settle();
+    int jt = 0;
+    for (; jt + 1 < last; jt += 2) {
+      fetch(k1s, v1s, jt + 1);
+      compute(k0s, v0s, jt * BC, std::false_type{});
+      settle();
+      fetch(k0s, v0s, jt + 2);
+      compute(k1s, v1s, (jt + 1) * BC, std::false_type{});
+      settle();
+    }
+    if (jt < last) {  // tile last - 1 in buffer 0, the last one goes to buffer 1
+      fetch(k1s, v1s, last);
+      compute(k0s, v0s, jt * BC, std::false_type{});
+      settle();
+      compute(k1s, v1s, last * BC, std::true_type{});
+    } else {  // the last tile is in buffer 0
+      compute(k0s, v0s, last * BC, std::true_type{});
+    }
   }
 
   if (qrow < n) {
