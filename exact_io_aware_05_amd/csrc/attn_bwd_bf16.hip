@@ -602,13 +602,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   const int kend = CAUSAL ? min(nk, q0 + BR + coff) : nk;
   const int ntiles = kend > 0 ? (kend + BC - 1) / BC : 0;
 
-  // TAIL: the tile may hold keys past nk (only the last tile can); the full
-  // mask path masks them only in such calls.
+  // TAIL: the tile may need masking (keys past nk, or under causal keys
+  // after some row of the wave) or be skipped by some wave; calls without it
+  // are for tiles every key of which every row of the workgroup sees.
   auto compute = [&](const uint16_t* ks, const uint16_t* vs, int j0, auto tail) ATTN_INLINE {
     constexpr bool TAIL = decltype(tail)::value;
-    const bool active = !CAUSAL || (j0 <= wq0 + 31 + coff);
+    const bool active = !TAIL || !CAUSAL || (j0 <= wq0 + 31 + coff);
     if (!active) return;
-    const bool need_mask = (j0 + BC > nk) || (CAUSAL && j0 + BC - 1 > wq0 + coff);
+    const bool need_mask = TAIL && ((j0 + BC > nk) || (CAUSAL && j0 + BC - 1 > wq0 + coff));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       // One half tile at a time: interleaving the halves costs more
@@ -670,7 +671,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pv = fast_exp2(fmaf(sacc[r], sl2e, -l2));
-          if (TAIL && need_mask) pv = (j0 + 32 * t + crow(r, hh) >= nk) ? 0.f : pv;
+          if (need_mask) pv = (j0 + 32 * t + crow(r, hh) >= nk) ? 0.f : pv;
           ds[r] = pv * dpd_of(r);
         }
       }
@@ -742,39 +743,16 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
       wait_vmem();
       __syncthreads();
     }
-  } else if constexpr (CAUSAL) {
-    // Causal: every tile may need the diagonal mask (a branch inside
-    // compute), and two call sites keep the loop within the register file.
-    if (ntiles > 0) {
-      dma_tile<D, NW>(rk, k0s, 0, w, lane);
-      dma_tile<D, NW>(rv, v0s, 0, w, lane);
-      wait_vmem();
-      __syncthreads();
-    }
-    for (int jt = 0; jt < ntiles; jt += 2) {
-      if (jt + 1 < ntiles) {
-        dma_tile<D, NW>(rk, k1s, (jt + 1) * BC, w, lane);
-        dma_tile<D, NW>(rv, v1s, (jt + 1) * BC, w, lane);
-      }
-      compute(k0s, v0s, jt * BC, std::true_type{});
-      wait_vmem();
-      __syncthreads();
-      if (jt + 1 >= ntiles) break;
-      if (jt + 2 < ntiles) {
-        dma_tile<D, NW>(rk, k0s, (jt + 2) * BC, w, lane);
-        dma_tile<D, NW>(rv, v0s, (jt + 2) * BC, w, lane);
-      }
-      compute(k1s, v1s, (jt + 1) * BC, std::true_type{});
-      wait_vmem();
-      __syncthreads();
-    }
   } else if (ntiles > 0) {
-    // Tiles 0 .. last - 1 in pairs (buffer 0, buffer 1), each pair fetching
-    // the next two, with no exit inside the pair: a loop that could leave
-    // between its two halves made the register allocator copy the dQ
-    // accumulators on every tile.  The last tile (the only one that can
-    // hold keys past nk) follows the loop.
-    const int last = ntiles - 1;
+    // Tiles 0 .. nfree - 1 need no mask and no skip (full mask: all but the
+    // last tile, the only one that can hold keys past nk; causal: the tiles
+    // whose keys all precede the workgroup's first row).  They run in pairs
+    // (buffer 0, buffer 1), each pair fetching the next two, with no exit
+    // inside the pair: a loop that could leave between its two halves made
+    // the register allocator copy the dQ accumulators on every tile.  The
+    // remaining tiles (the last one, or the diagonal ones) follow in a loop
+    // with the checks.
+    const int nfree = CAUSAL ? min(ntiles, max(0, (q0 + coff + 1) / BC)) : ntiles - 1;
     auto fetch = [&](uint16_t* ks, uint16_t* vs, int jt) ATTN_INLINE {
       dma_tile<D, NW>(rk, ks, jt * BC, w, lane);
       dma_tile<D, NW>(rv, vs, jt * BC, w, lane);
@@ -786,7 +764,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
     fetch(k0s, v0s, 0);
     settle();
     int jt = 0;
-    for (; jt + 1 < last; jt += 2) {
+    for (; jt + 1 < nfree && jt + 2 < ntiles; jt += 2) {
       fetch(k1s, v1s, jt + 1);
       compute(k0s, v0s, jt * BC, std::false_type{});
       settle();
@@ -794,13 +772,24 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
       compute(k1s, v1s, (jt + 1) * BC, std::false_type{});
       settle();
     }
-    if (jt < last) {  // tile last - 1 in buffer 0, the last one goes to buffer 1
-      fetch(k1s, v1s, last);
+    // Tile jt is in buffer 0.
+    if constexpr (CAUSAL) {
+      for (; jt < ntiles; jt += 2) {
+        if (jt + 1 < ntiles) fetch(k1s, v1s, jt + 1);
+        compute(k0s, v0s, jt * BC, std::true_type{});
+        if (jt + 1 >= ntiles) break;
+        settle();
+        if (jt + 2 < ntiles) fetch(k0s, v0s, jt + 2);
+        compute(k1s, v1s, (jt + 1) * BC, std::true_type{});
+        settle();
+      }
+    } else if (jt + 1 < ntiles) {  // tiles last - 1 (buffer 0) and last
+      fetch(k1s, v1s, jt + 1);
       compute(k0s, v0s, jt * BC, std::false_type{});
       settle();
-      compute(k1s, v1s, last * BC, std::true_type{});
-    } else {  // the last tile is in buffer 0
-      compute(k0s, v0s, last * BC, std::true_type{});
+      compute(k1s, v1s, (jt + 1) * BC, std::true_type{});
+    } else {  // the last tile, in buffer 0
+      compute(k0s, v0s, jt * BC, std::true_type{});
     }
   }
 
