@@ -565,9 +565,17 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   const int l32 = lane & 31, hh = lane >> 5;
   const TileReader<D> TR(lane);
 
-  const int lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / nqb;
-  const int qb = CAUSAL ? (nqb - 1 - lid % nqb) : (lid % nqb);
+  // Under the causal mask heavy (late) query blocks first, longest first
+  // within each XCD.
+  int bh, qi;
+  if (CAUSAL) {
+    heavy_first(blockIdx.x, total / nqb, nqb, bh, qi);
+  } else {
+    const int lid = xcd_remap(blockIdx.x, total);
+    bh = lid / nqb;
+    qi = lid % nqb;
+  }
+  const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
   const int q0 = qb * BR;
   const int wq0 = q0 + 32 * w;
   const int qrow = wq0 + l32;

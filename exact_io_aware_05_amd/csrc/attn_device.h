@@ -178,4 +178,27 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
   return x * q + (x < r ? x : r) + k;
 }
 
+// Causal workgroup order: longest first within each XCD.  Under the causal
+// mask the work of a query block grows with its index, and a workgroup
+// order that walks one head's blocks heavy to light, head after head,
+// leaves an XCD's last CUs with heavy blocks at the end.  When the head
+// count is a multiple of 8, XCD x (hardware id % 8) owns heads x * hx ..
+// x * hx + hx - 1 (hx = heads / 8, so a head's blocks share one L2) and
+// takes them rank-major: rank 0 (the heaviest block) of each of its heads,
+// then rank 1, and so on.  Every XCD receives exactly hx * nblk ids, so the
+// map is a bijection of [0, heads * nblk).  Otherwise the xcd_remap order
+// (head-major) is kept.
+__device__ __forceinline__ void heavy_first(int pid, int heads, int nblk, int& bh, int& rank) {
+  if ((heads & 7) == 0) {
+    const int hx = heads >> 3;
+    const int x = pid & 7, s = pid >> 3;
+    rank = s / hx;
+    bh = x * hx + s % hx;
+  } else {
+    const int lid = xcd_remap(pid, heads * nblk);
+    bh = lid / nblk;
+    rank = lid % nblk;
+  }
+}
+
 }  // namespace attn

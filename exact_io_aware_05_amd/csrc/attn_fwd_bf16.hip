@@ -86,16 +86,22 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   const TileReader<D> TRK(lane);
   const TileReader<D> TRV(lane);
 
-  // Logical tile: contiguous per XCD; heavy (late) query blocks first.
-  // Unequal lengths (QK): n is the query length, nk the key length; with
-  // split-K/V a workgroup owns one query block and one chunk of keys.
+  // Logical tile: contiguous per XCD; under the causal mask heavy (late)
+  // query blocks first, longest first within each XCD.  Unequal lengths
+  // (QK): n is the query length, nk the key length; with split-K/V a
+  // workgroup owns one query block and one chunk of keys.
   const int nsplit = QK ? qa.nsplit : 1;
-  const int lid = xcd_remap(blockIdx.x, total);
-  const int per_head = nqb * nsplit;
-  const int bh = lid / per_head;
-  const int rem = lid % per_head;
-  const int qi = QK ? rem / nsplit : rem;
-  const int sp = QK ? rem % nsplit : 0;
+  int bh, qi, sp = 0;
+  if (CAUSAL && nsplit == 1) {
+    heavy_first(blockIdx.x, total / nqb, nqb, bh, qi);
+  } else {
+    const int lid = xcd_remap(blockIdx.x, total);
+    const int per_head = nqb * nsplit;
+    bh = lid / per_head;
+    const int rem = lid % per_head;
+    qi = QK ? rem / nsplit : rem;
+    sp = QK ? rem % nsplit : 0;
+  }
   const int qb = CAUSAL ? (nqb - 1 - qi) : qi;
   const int q0 = qb * BR;
   const int nk = QK ? qa.nk : n;
