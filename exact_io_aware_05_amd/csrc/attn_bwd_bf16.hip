@@ -78,10 +78,10 @@ __device__ __forceinline__ void pipeline_reads() {
   __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
 }
 
-// Same, for MFMAs whose operand takes two reads.
-template <int M>
+// Same, for MFMAs whose operand takes two reads; AHEAD MFMAs' operands are
+// read before the first MFMA.
+template <int M, int AHEAD = M / 2>
 __device__ __forceinline__ void pipeline_reads2() {
-  constexpr int AHEAD = M / 2;
   __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
 #pragma unroll
   for (int i = 0; i < M - AHEAD; ++i) {
@@ -213,13 +213,15 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     dma_tile_asm<D, NW>(rq, q_at(b), i * BQ, w, lane);
     dma_tile_asm<D, NW>(rdo, g_at(b), i * BQ, w, lane);
   };
-  // Wave 0 scales the landed LSE row of buffer b to base 2, in place; the
-  // tiles fetched after it (LATER loads) may still be in flight.
+  // Wave 0 scales the landed LSE row of buffer b to base 2 and negates the
+  // D row, in place; the tiles fetched after them (LATER loads) may still be
+  // in flight.
   auto fix_small = [&](auto b, auto later) ATTN_INLINE {
     if (w == 0) {
       wait_vmem_upto<decltype(later)::value>();
       asm volatile("" ::: "memory");
       lse_at(b)[lane] *= kLog2e;
+      dsm_at(b)[lane] = -dsm_at(b)[lane];
     }
   };
   // End of a tile: the batch of the next tile must have landed; the batch
@@ -293,6 +295,25 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 #pragma unroll
     for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[1][e], h[1], acc[e]);
     pipeline_reads2<D / 16>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The products of both half tiles (operands h0 for queries 0-31, h1 for
+  // 32-63) as one stream of 4 D / 16 MFMAs, so that operand reads run ahead
+  // across the two halves instead of stalling at the start of each.
+  auto acc_pair = [&](auto& tr, const uint16_t* bs, const bf16x8* h0, const bf16x8* h1) ATTN_INLINE {
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 a[4][D / 32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) a[q][e] = tr.cols(bs, 16 * q, e);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bf16x8& hq = q < 2 ? h0[q & 1] : h1[q & 1];
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[q][e], hq, acc[e]);
+    }
+    pipeline_reads2<D / 8, 4>();
     __builtin_amdgcn_sched_barrier(0);
   };
   // Wave-uniform test for the split.  P enters dV as it is; dS enters dK
@@ -433,18 +454,21 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
       }
       mid();
       if (act) {
-        // hi terms always, lo terms only where the half tile needs them: the
-        // accumulators are only ever updated in place (no alternative paths
-        // that the register allocator would join with copies).
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 h[2] = {pack_bf16x8(v[t]), pack_bf16x8(v[t] + 8)};
-          const bool sp = needs_split(v[t]);
-          acc_plain(TR, g_at(b), h, t);
-          if (sp) {
-            const bf16x8 l[2] = {split_lo_bf16x8(v[t], h[0]), split_lo_bf16x8(v[t] + 8, h[1])};
-            acc_plain(TR, g_at(b), l, t);
-          }
+        // hi terms always (both halves as one stream), lo terms only where
+        // the half tile needs them: the accumulators are only ever updated in
+        // place (no alternative paths that the register allocator would join
+        // with copies).
+        const bf16x8 h0[2] = {pack_bf16x8(v[0]), pack_bf16x8(v[0] + 8)};
+        const bf16x8 h1[2] = {pack_bf16x8(v[1]), pack_bf16x8(v[1] + 8)};
+        const bool sp0 = needs_split(v[0]), sp1 = needs_split(v[1]);
+        acc_pair(TR, g_at(b), h0, h1);
+        if (sp0) {
+          const bf16x8 l[2] = {split_lo_bf16x8(v[0], h0[0]), split_lo_bf16x8(v[0] + 8, h0[1])};
+          acc_plain(TR, g_at(b), l, 0);
+        }
+        if (sp1) {
+          const bf16x8 l[2] = {split_lo_bf16x8(v[1], h1[0]), split_lo_bf16x8(v[1] + 8, h1[1])};
+          acc_plain(TR, g_at(b), l, 1);
         }
       }
     });
@@ -458,17 +482,19 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     bf16x8 dhi[2][2], dlo[2][2];
     bool pend = false, spl0 = false, spl1 = false;
     auto deferred = [&](const uint16_t* qs) ATTN_INLINE {
-      acc_plain(TR, qs, dhi[0], 0);
-      acc_plain(TR, qs, dhi[1], 1);
+      acc_pair(TR, qs, dhi[0], dhi[1]);
       if (spl0) acc_plain(TR, qs, dlo[0], 0);
       if (spl1) acc_plain(TR, qs, dlo[1], 1);
     };
     run([&](auto b, int i, auto&& mid) ATTN_INLINE {
       constexpr int BP = (decltype(b)::value + 2) % 3;  // buffer of the previous tile
-      if (pend) deferred(q_at(int_c<BP>{}));
       const bool act = active(i);
+      // The accumulators start from -D (with dropout from 0: dP is needed
+      // alone, dS = P (Z dP / (1 - p) - D)).  The -D rows are read before
+      // the deferred products, which hide the LDS latency; read just before
+      // the chains, the first product waited for them.
       f32x16 c0, c1;
-      if (act) {
+      {
         const float* dsms = dsm_at(b);
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -476,13 +502,13 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
           const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dsms[32 + 8 * g + 4 * hh]);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
-            // With dropout dP is needed alone (dS = P (Z dP / (1 - p) - D)).
-            c0[4 * g + k] = DROP ? 0.f : -d0[k];
-            c1[4 * g + k] = DROP ? 0.f : -d1[k];
+            c0[4 * g + k] = DROP ? 0.f : d0[k];
+            c1[4 * g + k] = DROP ? 0.f : d1[k];
           }
         }
-        chains(TR, g_at(b), c0, c1);
       }
+      if (pend) deferred(q_at(int_c<BP>{}));
+      if (act) chains(TR, g_at(b), c0, c1);
       mid();
       pend = act;
       if (act) {
@@ -498,7 +524,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
               for (int k = 0; k < 4; ++k) {
                 const float dpv = t == 0 ? c0[4 * g + k] : c1[4 * g + k];
                 const bool kept = (__float_as_uint(p4[k]) >> 31) == 0u;
-                v[4 * g + k] = fabsf(p4[k]) * ((kept ? dpv * dr.keep_scale : 0.f) - d4[k]);
+                v[4 * g + k] = fabsf(p4[k]) * ((kept ? dpv * dr.keep_scale : 0.f) + d4[k]);  // d4 = -D
               }
             } else {
 #pragma unroll
