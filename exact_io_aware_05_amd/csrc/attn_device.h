@@ -184,16 +184,33 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
 // leaves an XCD's last CUs with heavy blocks at the end.  When the head
 // count is a multiple of 8, XCD x (hardware id % 8) owns heads x * hx ..
 // x * hx + hx - 1 (hx = heads / 8, so a head's blocks share one L2) and
-// takes them rank-major: rank 0 (the heaviest block) of each of its heads,
-// then rank 1, and so on.  Every XCD receives exactly hx * nblk ids, so the
-// map is a bijection of [0, heads * nblk).  Otherwise the xcd_remap order
-// (head-major) is kept.
+// takes them in groups of up to four heads, each group rank-major: rank 0
+// (the heaviest block) of its heads, then rank 1, and so on (a last group
+// may be smaller).  All hx heads rank-major at once kept every head's keys
+// and values in flight and fetched 3x the minimum from HBM (B=4 H=16 N=4096
+// forward); groups of four fetch 1.5x and run as fast; groups of two fetch
+// the minimum but run 2-3% slower.
+// Every XCD receives exactly hx * nblk ids, so the map is a bijection of
+// [0, heads * nblk).  Otherwise the xcd_remap order (head-major) is kept.
 __device__ __forceinline__ void heavy_first(int pid, int heads, int nblk, int& bh, int& rank) {
   if ((heads & 7) == 0) {
     const int hx = heads >> 3;
     const int x = pid & 7, s = pid >> 3;
-    rank = s / hx;
-    bh = x * hx + s % hx;
+    const int g = hx >= 4 ? 4 : hx;  // heads per group
+    const int full = hx / g;         // groups of g heads
+    const int span = g * nblk;       // ids per full group
+    int grp, sub, gl;
+    if (s < full * span) {
+      grp = s / span;
+      sub = s - grp * span;
+      gl = g;
+    } else {
+      grp = full;
+      sub = s - full * span;
+      gl = hx - full * g;
+    }
+    rank = sub / gl;
+    bh = x * hx + grp * g + (sub - rank * gl);
   } else {
     const int lid = xcd_remap(pid, heads * nblk);
     bh = lid / nblk;

@@ -67,14 +67,15 @@ def test_backward_small_shapes(shape, causal, dtype):
     assert_close(dv, dv_r, dtype, "dV")
 
 
-@pytest.mark.parametrize("d", [64, 128])
-def test_causal_head_count_multiple_of_eight(d):
+@pytest.mark.parametrize("b,d", [(2, 64), (2, 128), (6, 64)])
+def test_causal_head_count_multiple_of_eight(b, d):
     # With B * H a multiple of 8 the causal kernels order their workgroups
-    # longest first per XCD (a different map from blocks to workgroups than
-    # other head counts): every output element against the oracle.
-    shape = (2, 8, 520, d)
-    seed = 2400 + d
-    _announce("fwd+bwd causal, 16 heads", shape, "seed", seed)
+    # longest first per XCD, in groups of up to four heads (a different map
+    # from blocks to workgroups than other head counts; 48 heads leave each
+    # XCD a last group of two): every output element against the oracle.
+    shape = (b, 8, 520, d)
+    seed = 2400 + d + b
+    _announce("fwd+bwd causal", b * 8, "heads", shape, "seed", seed)
     inp = synth.qkvdo(seed, shape, "bf16")
     scale = 1.0 / math.sqrt(d)
     o, lse, dq, dk, dv = _run(inp, "bf16", True, scale)
