@@ -15,16 +15,17 @@
 //    LDS; two waves share each 32-key group (one for S, P and dV, one for
 //    dP, dS and dK).  S and dP use the C[q][key] layout (lane = key,
 //    registers run over queries), so P and dS feed dV^T += dO^T P and
-//    dK^T += Q^T dS straight from registers as the B operand, each as a
-//    hi + lo pair of bf16 values.  dO^T and Q^T are read from the row-major
-//    tiles with transposing LDS reads.
+//    dK^T += Q^T dS straight from registers as the B operand, as bf16
+//    values (hi + lo pairs on half tiles where a term's weight reaches
+//    1/16).  dO^T and Q^T are read from the row-major tiles with transposing
+//    LDS reads.
 //  * bwd_q: a workgroup owns a block of queries (32 per wave) with Q, dO,
 //    LSE and D in registers and streams key tiles of 64 rows: S^T = K Q^T and
 //    dP^T = V dO^T (lane = query), dS^T, then dQ^T += K^T dS^T, with K^T
 //    read transposed from the row-major K tile.
-// Tiles come from buffer->LDS DMA into two buffers (the next tile streams in
-// while the current one is used; rows past the end of the head arrive as
-// zeros).
+// Tiles come from buffer->LDS DMA, into three buffers in bwd_kv (the tile
+// after next streams in while the current one is used) and two in bwd_q;
+// rows past the end of the head arrive as zeros.
 #include <type_traits>
 
 #include "attn_device.h"

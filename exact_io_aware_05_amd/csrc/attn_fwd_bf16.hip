@@ -38,7 +38,9 @@
 //    whose m is still -inf (nothing seen yet) always takes that path.
 //  * Causal: key tiles beyond the workgroup's last query are never visited;
 //    units wholly above a wave's rows are skipped by that wave; masking code
-//    runs only on diagonal and ragged-tail units, which come last.
+//    runs only on diagonal and ragged-tail units, which come last.  The
+//    heavy query blocks are scheduled first, longest first within each XCD
+//    (heavy_first in attn_device.h).
 #include "attn_device.h"
 #include "attn_launch.h"
 #include "attn_tile.h"
