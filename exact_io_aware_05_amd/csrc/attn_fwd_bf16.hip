@@ -463,7 +463,14 @@ template <bool SPARSE, bool QK>
 static hipError_t fwd_bf16_t(const FwdArgs& a) {
   if (a.d == 64)
     return a.causal ? launch_fwd<64, 4, true, SPARSE, QK>(a) : launch_fwd<64, 4, false, SPARSE, QK>(a);
-  return a.causal ? launch_fwd<128, 4, true, SPARSE, QK>(a) : launch_fwd<128, 4, false, SPARSE, QK>(a);
+  // d = 128, dense: eight waves (256 query rows) share each K/V tile, which
+  // halves the fetch's LDS writes per query (3.3% faster at N = 4096; at
+  // d = 64 eight waves are 6% slower).  Block-sparse workgroups stay one
+  // 128-row mask block; unequal lengths keep four waves.
+  if constexpr (!SPARSE && !QK)
+    return a.causal ? launch_fwd<128, 8, true, false, false>(a) : launch_fwd<128, 8, false, false, false>(a);
+  else
+    return a.causal ? launch_fwd<128, 4, true, SPARSE, QK>(a) : launch_fwd<128, 4, false, SPARSE, QK>(a);
 }
 
 hipError_t fwd_bf16(const FwdArgs& a) {
