@@ -422,23 +422,39 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
           c1[r] = 0.f;
         }
         chains(TR, q_at(b), c0, c1);
-        const bool need_mask = CAUSAL && (i * BQ < kw0 + 31 - coff);
+        // Exponent arguments; on the diagonal tiles only (a wave-uniform
+        // branch), entries whose key follows the query become -inf, whose
+        // exp2 is 0.  Written as selects inside the exponential loop, the
+        // mask ran on every tile.
+        float x[2][16];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * t + 8 * g + 4 * hh]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) x[t][4 * g + k] = fmaf(t == 0 ? c0[4 * g + k] : c1[4 * g + k], sl2e, -l4[k]);
+          }
+        if (CAUSAL && i * BQ < kw0 + 31 - coff) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int q = i * BQ + 32 * t + crow(r, hh);
+              x[t][r] = key > q + coff ? -INFINITY : x[t][r];
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
             const int qbase = i * BQ + 32 * t + 8 * g + 4 * hh;  // queries qbase + k of registers 4g + k
             uint32_t keep = 0xFu;
             if constexpr (DROP) keep = quad_keep(qbase);
             f32x4 o;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-              float pv = fast_exp2(fmaf(t == 0 ? c0[4 * g + k] : c1[4 * g + k], sl2e, -l4[k]));
-              if (need_mask) {
-                const int q = qbase + k;
-                pv = key > q + coff ? 0.f : pv;
-              }
+              const float pv = fast_exp2(x[t][4 * g + k]);
               if constexpr (DROP) {
                 // dV takes the dropped, rescaled probability; the dP wave
                 // gets P with the keep bit in the sign (P >= 0).
