@@ -250,7 +250,7 @@ def main():
 
     if args.gpus != 1:
         print(
-            f"bench.py: --gpus {args.gpus} requested; this build runs on one GPU only "
+            f"bench.py: --gpus {args.gpus} requested; the library runs on one GPU only "
             "(the kernels work on one device's share and there is no multi-GPU path)",
             file=sys.stderr,
         )
