@@ -83,6 +83,23 @@ SplitPlan split_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int num_split
   return SplitPlan{(int)ns, (int)(tiles_per * 64)};
 }
 
+// Split of the backward's dQ pass over keys (unequal lengths): with few
+// (head, query block) workgroups, enough chunks to give the chip about two
+// workgroups per CU (256 CUs), each chunk at least 4 tiles.
+SplitPlan dq_split_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+  const int64_t ktiles = (Nk + 63) / 64;
+  const int64_t rows = attn::bwd_dq_rows(d);
+  const int64_t wgs = B * H * ((Nq + rows - 1) / rows);
+  int64_t want = (512 + wgs - 1) / wgs;
+  want = want < ktiles / 4 ? want : ktiles / 4;
+  if (want > 64) want = 64;
+  if (want < 2) return SplitPlan{1, (int)(ktiles * 64)};
+  const int64_t tiles_per = (ktiles + want - 1) / want;
+  const int64_t ns = (ktiles + tiles_per - 1) / tiles_per;
+  if (ns < 2) return SplitPlan{1, (int)(ktiles * 64)};
+  return SplitPlan{(int)ns, (int)(tiles_per * 64)};
+}
+
 int check_qk(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype) {
   int st = check_shape(B, H, Nq, d, dtype);
   if (st != ATTN_OK) return st;
@@ -355,7 +372,10 @@ int attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse
 
 size_t attn_bwd_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype) {
   if (check_qk(B, H, Nq, Nk, d, dtype) != ATTN_OK) return 0;
-  return align256((size_t)(B * H * Nq) * sizeof(float));
+  const size_t dbytes = align256((size_t)(B * H * Nq) * sizeof(float));
+  const SplitPlan sp = dq_split_plan(B, H, Nq, Nk, d);
+  if (sp.nsplit < 2) return dbytes;
+  return dbytes + align256((size_t)sp.nsplit * (size_t)(B * H * Nq) * (size_t)d * sizeof(float));
 }
 
 int attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -371,6 +391,12 @@ int attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, cons
   attn::BwdArgs a =
       make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, Nq, d, causal, scale, stream);
   a.nk = Nk;
+  const SplitPlan sp = dq_split_plan(B, H, Nq, Nk, d);
+  if (sp.nsplit > 1) {
+    a.nsplit = sp.nsplit;
+    a.kchunk = sp.kchunk;
+    a.dqpart = (float*)((char*)workspace + align256((size_t)(B * H * Nq) * sizeof(float)));
+  }
   if (attn::bwd_dsum(a, true) != hipSuccess) return ATTN_E_HIP;
   if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
   if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;

@@ -26,6 +26,7 @@
 // Tiles come from buffer->LDS DMA, into three buffers in bwd_kv (the tile
 // after next streams in while the current one is used) and two in bwd_q;
 // rows past the end of the head arrive as zeros.
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_device.h"
@@ -594,7 +595,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
                                                            uint16_t* __restrict__ dQ, int n, int nqb, int total,
                                                            float scale, float sl2e,
                                                            const uint8_t* __restrict__ bmask, long long mask_stride,
-                                                           int nb, int nk_arg, int coff_arg, DropArgs dr) {
+                                                           int nb, int nk_arg, int coff_arg, DropArgs dr,
+                                                           int kchunk, float* __restrict__ dqpart) {
   constexpr int BR = NW * 32, BC = 64;
 
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[BC * D];
@@ -608,13 +610,21 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   const int l32 = lane & 31, hh = lane >> 5;
   const TileReader<D> TR(lane);
 
+  // Unequal lengths, split over keys: the grid holds one copy of the
+  // (head, query block) items per chunk of kchunk keys.
+  const bool split = QK && dqpart != nullptr;
+  int bid = blockIdx.x, ks = 0;
+  if (split) {
+    ks = bid / total;
+    bid -= ks * total;
+  }
   // Under the causal mask heavy (late) query blocks first, longest first
   // within each XCD.
   int bh, qi;
   if (CAUSAL) {
-    heavy_first(blockIdx.x, total / nqb, nqb, bh, qi);
+    heavy_first(bid, total / nqb, nqb, bh, qi);
   } else {
-    const int lid = xcd_remap(blockIdx.x, total);
+    const int lid = xcd_remap(bid, total);
     bh = lid / nqb;
     qi = lid % nqb;
   }
@@ -624,11 +634,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   const int qrow = wq0 + l32;
 
   // Unequal lengths (QK): n is the query length, nk the key length, and
-  // query i sees key j when j <= i + coff (causal, bottom-right).
-  const int nk = QK ? nk_arg : n;
-  const int coff = (QK && CAUSAL) ? coff_arg : 0;
+  // query i sees key j when j <= i + coff (causal, bottom-right).  A chunk
+  // of the split is the same problem on keys kb .. kb + nk - 1: K and V start
+  // kb rows later and the causal offset drops by kb (rows that see no key of
+  // the chunk get a zero partial).
+  const int kb = split ? ks * kchunk : 0;
+  const int nk = QK ? (split ? min(kchunk, nk_arg - kb) : nk_arg) : n;
+  const int coff = (QK && CAUSAL) ? coff_arg - kb : 0;
   const size_t head = (size_t)bh * (size_t)n * D;
-  const size_t khead = (size_t)bh * (size_t)nk * D;
+  const size_t khead = (size_t)bh * (size_t)(QK ? nk_arg : n) * D + (size_t)kb * D;
   const uint32_t head_bytes = (uint32_t)n * D * 2u;
   const auto rq = make_rsrc(Q + head, head_bytes);
   const auto rdo = make_rsrc(dO + head, head_bytes);
@@ -844,7 +858,18 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
     }
   }
 
-  if (qrow < n) {
+  if (split && qrow < n) {
+    float* prow = dqpart + ((size_t)ks * (size_t)(total / nqb) * (size_t)n * D) + head + (size_t)qrow * D;
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = dqa[e][4 * g + i] * scale;
+        *reinterpret_cast<f32x4*>(prow + 32 * e + 8 * g + 4 * hh) = o4;
+      }
+  } else if (qrow < n) {
     uint16_t* drow = dQ + head + (size_t)qrow * D;
 #pragma unroll
     for (int e = 0; e < D / 32; ++e)
@@ -855,6 +880,26 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
         o2[1] = pack_bf16x2(dqa[e][4 * g + 2] * scale, dqa[e][4 * g + 3] * scale);
         *reinterpret_cast<u32x2*>(drow + 32 * e + 8 * g + 4 * hh) = o2;
       }
+  }
+}
+
+// Sum of the split dQ partials, chunk 0 first (a fixed order: the result does
+// not depend on scheduling), rounded once to bf16 (nearest-even).  Four
+// consecutive features per thread; the partials of chunk s start s * n4
+// vectors after those of chunk 0.
+__global__ __launch_bounds__(256) void dq_merge_kernel(const f32x4* __restrict__ part, uint16_t* __restrict__ dq,
+                                                       long long n4, int nsplit) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long long)gridDim.x * 256) {
+    f32x4 acc = part[i];
+    for (int s = 1; s < nsplit; ++s) {
+      const f32x4 v = part[i + (long long)s * n4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += v[c];
+    }
+    u32x2 o2;
+    o2[0] = pack_bf16x2(acc[0], acc[1]);
+    o2[1] = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<u32x2*>(dq + 4 * i) = o2;
   }
 }
 
@@ -885,10 +930,17 @@ hipError_t launch_dq(const BwdArgs& a) {
   const int total = (int)(a.bh * nqb);
   const int nb = (n + kSparseBlock - 1) / kSparseBlock;
   const int nk = QK ? (int)a.nk : n;
-  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK, DROP>), dim3(total), dim3(NW * 64), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
-                     a.lse, a.dsum, (uint16_t*)a.dq, n, nqb, total, a.scale, a.scale * kLog2e, a.bmask,
-                     (long long)a.mask_stride, nb, nk, nk - n, a.drop);
+  const bool split = QK && a.nsplit > 1;
+  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK, DROP>), dim3(total * (split ? a.nsplit : 1)),
+                     dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                     (const uint16_t*)a.dout, a.lse, a.dsum, (uint16_t*)a.dq, n, nqb, total, a.scale,
+                     a.scale * kLog2e, a.bmask, (long long)a.mask_stride, nb, nk, nk - n, a.drop,
+                     split ? a.kchunk : 0, split ? a.dqpart : nullptr);
+  if (!split) return hipGetLastError();
+  const long long n4 = a.bh * a.n * (long long)D / 4;
+  const long long blocks = std::min<long long>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(dq_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, a.stream, (const f32x4*)a.dqpart,
+                     (uint16_t*)a.dq, n4, a.nsplit);
   return hipGetLastError();
 }
 
@@ -915,6 +967,8 @@ hipError_t bwd_bf16_dkdv(const BwdArgs& a) {
   if (a.nk >= 0) return dkdv_t<false, true>(a);
   return dkdv_t<false, false>(a);
 }
+
+int bwd_dq_rows(int64_t d) { return d == 128 ? 32 * ATTN_DQ_NW128 : 128; }
 
 hipError_t bwd_bf16_dq(const BwdArgs& a) {
   if (a.dropout) {

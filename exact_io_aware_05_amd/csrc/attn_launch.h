@@ -79,9 +79,16 @@ struct BwdArgs {
   hipStream_t stream;
   const uint8_t* bmask = nullptr;  // as in FwdArgs
   int64_t mask_stride = 0;
-  int64_t nk = -1;  // as in FwdArgs (no split in the backward)
+  int64_t nk = -1;  // as in FwdArgs
   bool dropout = false;
   DropArgs drop;
+  // Unequal lengths: the dQ pass split over nsplit chunks of kchunk keys
+  // (whole 64-key tiles); chunk s writes its fp32 partial dQ (scale
+  // applied) to dqpart[s][bh][n][d], and a second kernel sums the chunks in
+  // order into dq.  nsplit = 1: no split, dqpart unused.
+  int nsplit = 1;
+  int kchunk = 0;
+  float* dqpart = nullptr;
 };
 
 // Block size of the block-sparse mask (query and key rows per block).
@@ -96,6 +103,8 @@ hipError_t fwd_f32(const FwdArgs& a);
 hipError_t bwd_dsum(const BwdArgs& a, bool bf16);
 hipError_t bwd_bf16_dkdv(const BwdArgs& a);
 hipError_t bwd_bf16_dq(const BwdArgs& a);
+// Query rows per dQ workgroup of the bf16 kernels for head dimension d.
+int bwd_dq_rows(int64_t d);
 hipError_t bwd_f32_dkdv(const BwdArgs& a);
 hipError_t bwd_f32_dq(const BwdArgs& a);
 

@@ -120,3 +120,60 @@ def test_equal_lengths_match_square_path_bitwise(d, causal):
     torch.cuda.synchronize()
     for a, b in zip((o1, l1) + tuple(g1), (o2, l2) + tuple(g2)):
         assert torch.equal(a, b)
+
+
+def _dsum_bytes(B, H, nq):
+    return -(-(B * H * nq * 4) // 256) * 256
+
+
+# (B, H, Nq, Nk, d): decoding (one query), a ragged last chunk, more queries
+# than keys (rows that see no key of some chunks, or none at all).
+SPLIT_CASES = [(2, 4, 1, 5000, 128), (1, 2, 300, 1030, 64), (1, 1, 700, 600, 128), (2, 2, 64, 4096, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", SPLIT_CASES)
+def test_backward_with_dq_split_over_keys(case, causal):
+    # Few (head, query block) workgroups: the library splits the dQ pass over
+    # key chunks and sums the fp32 partials; the workspace holds them.
+    E = _api()
+    B, H, nq, nk, d = case
+    assert E.lib().attn_bwd_qk_workspace_bytes(B, H, nq, nk, d, E.ATTN_BF16) > _dsum_bytes(B, H, nq)
+    seed = 6400 + nq + nk + d + causal
+    _announce("qk bwd, dQ split", case, "causal" if causal else "full", "seed", seed)
+    inp = _inputs(seed, B, H, nq, nk, d)
+    q, k, v, do = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = E.attn_fwd_qk(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv = E.attn_bwd_qk(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], causal, scale)
+    g_r = VL.backward_qk_batched(inp["q"], inp["k"], inp["v"], inp["do"], causal, scale)
+    _check_fwd(download(o), download(lse), o_r, lse_r)
+    empty = np.isneginf(lse_r)
+    assert np.all(download(dq)[empty] == 0)
+    assert_close(download(dq), g_r[0], "bf16", "dQ")
+    assert_close(download(dk), g_r[1], "bf16", "dK")
+    assert_close(download(dv), g_r[2], "bf16", "dV")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_chunked_prefill_backward_sampled_heads(causal):
+    # 1024 queries after 7168 cached tokens, 16 heads, d = 128: eight key
+    # chunks of 1024.  Two heads against the oracle, whole.
+    E = _api()
+    B, H, nq, nk, d = 1, 16, 1024, 8192, 128
+    assert E.lib().attn_bwd_qk_workspace_bytes(B, H, nq, nk, d, E.ATTN_BF16) == (
+        _dsum_bytes(B, H, nq) + 8 * B * H * nq * d * 4)
+    _announce("chunked prefill bwd", (B, H, nq, nk, d), "causal" if causal else "full")
+    inp = _inputs(6500 + causal, B, H, nq, nk, d)
+    q, k, v, do = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v", "do"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = E.attn_fwd_qk(q, k, v, causal=causal, scale=scale, num_splits=0)
+    dq, dk, dv = E.attn_bwd_qk(q, k, v, o, do, lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    got = [download(t) for t in (dq, dk, dv)]
+    for h in synth.sample_pairs(6510 + causal, H, 1, 2)[:, 0]:
+        g_r = VL.backward_qk(inp["q"][0, h], inp["k"][0, h], inp["v"][0, h], inp["do"][0, h], causal, scale)
+        for name, g, r in zip(("dQ", "dK", "dV"), got, g_r):
+            assert_close(g[0, h], r, "bf16", f"{name} (head {h})")
