@@ -9,7 +9,8 @@
 //   P = exp(scale*Q K^T - LSE), dV = P^T dO, dP = dO V^T,
 //   dS = P * (dP - D) with D_i = dO_i . O_i, dQ = scale dS K, dK = scale dS^T Q.
 //
-// Two kernels, neither uses atomics (deterministic results):
+// Two kernels (plus a merge for the split dQ), none uses atomics
+// (deterministic results):
 //  * bwd_kv: a workgroup owns 128 keys and keeps K, V and the dK, dV
 //    accumulators in registers while query tiles of 64 rows stream through
 //    LDS; two waves share each 32-key group (one for S, P and dV, one for
@@ -22,7 +23,10 @@
 //  * bwd_q: a workgroup owns a block of queries (32 per wave) with Q, dO,
 //    LSE and D in registers and streams key tiles of 64 rows: S^T = K Q^T and
 //    dP^T = V dO^T (lane = query), dS^T, then dQ^T += K^T dS^T, with K^T
-//    read transposed from the row-major K tile.
+//    read transposed from the row-major K tile.  With unequal lengths and
+//    few query blocks, the keys are split into chunks: each chunk's
+//    workgroups write fp32 partial dQ, and dq_merge adds the chunks in a
+//    fixed order (still deterministic).
 // Tiles come from buffer->LDS DMA, into three buffers in bwd_kv (the tile
 // after next streams in while the current one is used) and two in bwd_q;
 // rows past the end of the head arrive as zeros.
