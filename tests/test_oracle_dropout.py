@@ -6,14 +6,50 @@ the saved LSE, and the row identity behind D.  The generator is pinned by
 what a counter-based generator must satisfy: a bijection of the counter for a
 fixed key (no collisions), output bits that are uniform and that change by
 about half when one counter bit flips, keep rates within binomial bounds, and
-masks that change with the seed and the offset.
+masks that change with the seed and the offset.  Its identity with
+Philox4x32-10 is pinned by the published known-answer vectors
+(tests/golden/philox4x32_10_kat.json): a wrong multiplier, key increment,
+round count or word order fails them.
 """
+
+import json
+import os
 
 import numpy as np
 import pytest
 
 from oracle import attention as A
 from oracle import dropout as DR
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_philox_known_answer_vectors():
+    """The generator reproduces the published Philox4x32-10 known answers
+    (Salmon et al., SC 2011; the Random123 known-answer file): all-zero and
+    all-ones counters and keys, and the pi-digit counter and key."""
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
+        kat = json.load(f)
+    assert len(kat["vectors"]) == 3
+    for vec in kat["vectors"]:
+        c = [int(x, 16) for x in vec["counter"]]
+        k = [int(x, 16) for x in vec["key"]]
+        got = DR.philox4x32_10(*c, *k)
+        assert [int(np.asarray(w)) for w in got] == [int(x, 16) for x in vec["expected"]], vec
+
+
+def test_philox_known_answer_fails_a_planted_mistake(monkeypatch):
+    """The known answers catch a wrong constant: a planted change of the
+    second key increment (in the oracle, on the CPU) no longer reproduces the
+    pi-digit vector."""
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
+        vec = json.load(f)["vectors"][2]
+    c = [int(x, 16) for x in vec["counter"]]
+    k = [int(x, 16) for x in vec["key"]]
+    monkeypatch.setattr(DR, "_W1", DR._W1 ^ 1)
+    got = DR.philox4x32_10(*c, *k)
+    assert [int(np.asarray(w)) for w in got] != [int(x, 16) for x in vec["expected"]]
 
 
 def _r(shape, seed):
