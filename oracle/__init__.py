@@ -37,11 +37,10 @@ Modules:
 
 Every function here is pinned by ``tests/test_oracle*.py`` against page-printed
 values, closed forms, invariants, finite differences and a library autograd.
-One narrow exception: that ``oracle.dropout.philox4x32_10`` reproduces the
-published generator bit for bit is not pinned by a stored reference stream
-(no such stream is on the pages); its pins are the properties a counter-based
-generator must have (bijection, uniform bits, avalanche, keep rates).  This
-is "parity unpinned" for the generator's identity only; GPU masks are
+``oracle.dropout.philox4x32_10`` is pinned to the generator's published
+known-answer vectors (Salmon et al., SC 2011, as distributed with the
+authors' Random123 library), besides the properties a counter-based generator
+must have (bijection, uniform bits, avalanche, keep rates); GPU masks are
 compared with the oracle's bit for bit.
 """
 
