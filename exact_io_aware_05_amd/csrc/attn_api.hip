@@ -23,10 +23,21 @@ int check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Alignment the kernels rely on: tensors are read and written with 16-byte
+// vector and buffer->LDS accesses, the float32 row vectors (LSE, D) with
+// 4-byte ones.  A contiguous view at an odd element offset is a valid
+// pointer of its type and is still refused.
+bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+template <typename... P>
+bool all16(P... p) {
+  return (al16(p) && ...);
+}
+bool al4(const void* p) { return ((uintptr_t)p & 3) == 0; }
+
 // Block-sparse mask arguments (shape already validated): a mask, bf16, and a
 // head stride of 0 or at least nb * nb whose last head stays addressable.
 int check_mask(const uint8_t* mask, int64_t stride, int64_t B, int64_t H, int64_t N, int dtype) {
-  if (!mask) return ATTN_E_NULL;
+  if (!mask) return ATTN_E_NULL;  // read byte by byte: any alignment
   if (dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
   if (N > ATTN_SPARSE_MAX_N) return ATTN_E_SHAPE;  // the kernels list a row's tiles in LDS
   const int64_t nb = (N + ATTN_SPARSE_BLOCK - 1) / ATTN_SPARSE_BLOCK;
@@ -138,6 +149,7 @@ const char* attn_status_string(int status) {
     case ATTN_E_WORKSPACE: return "workspace missing or too small";
     case ATTN_E_HIP: return "HIP kernel launch failed";
     case ATTN_E_DROPOUT: return "dropout probability must lie in [0, 1)";
+    case ATTN_E_ALIGN: return "a tensor pointer is not 16-byte aligned (LSE and D: 4-byte)";
     default: return "unknown status";
   }
 }
@@ -145,6 +157,7 @@ const char* attn_status_string(int status) {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
              int64_t d, int dtype, int causal, float scale, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  if (!all16(q, k, v, o) || !al4(lse)) return ATTN_E_ALIGN;
   const int st = check_shape(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
   if (!isfinite(scale)) return ATTN_E_SCALE;
@@ -172,6 +185,7 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int 
 int attn_bwd_dsum(const void* o, const void* dout, float* dsum, int64_t B, int64_t H, int64_t N, int64_t d,
                   int dtype, void* stream) {
   if (!o || !dout || !dsum) return ATTN_E_NULL;
+  if (!all16(o, dout) || !al4(dsum)) return ATTN_E_ALIGN;
   const int st = check_shape(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
   attn::BwdArgs a = make_bwd(nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr, nullptr, dsum, B, H,
@@ -183,6 +197,7 @@ int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                   void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal, float scale,
                   void* stream) {
   if (!q || !k || !v || !dout || !lse || !dsum || !dk || !dv) return ATTN_E_NULL;
+  if (!all16(q, k, v, dout, dk, dv) || !al4(lse) || !al4(dsum)) return ATTN_E_ALIGN;
   const int st = check_shape(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
   if (!isfinite(scale)) return ATTN_E_SCALE;
@@ -196,6 +211,7 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, c
                 void* dq, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal, float scale,
                 void* stream) {
   if (!q || !k || !v || !dout || !lse || !dsum || !dq) return ATTN_E_NULL;
+  if (!all16(q, k, v, dout, dq) || !al4(lse) || !al4(dsum)) return ATTN_E_ALIGN;
   const int st = check_shape(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
   if (!isfinite(scale)) return ATTN_E_SCALE;
@@ -209,6 +225,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal,
              float scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  if (!all16(q, k, v, o, dout, dq, dk, dv) || !al4(lse)) return ATTN_E_ALIGN;
   const int st = check_shape(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
   if (!isfinite(scale)) return ATTN_E_SCALE;
@@ -228,6 +245,7 @@ int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, f
                          int64_t N, int64_t d, int dtype, int causal, float scale, const uint8_t* block_mask,
                          int64_t mask_head_stride, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  if (!all16(q, k, v, o) || !al4(lse)) return ATTN_E_ALIGN;
   int st = check_shape(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
   st = check_mask(block_mask, mask_head_stride, B, H, N, dtype);
@@ -255,6 +273,7 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
                          int dtype, int causal, float scale, const uint8_t* block_mask, int64_t mask_head_stride,
                          void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  if (!all16(q, k, v, o, dout, dq, dk, dv) || !al4(lse)) return ATTN_E_ALIGN;
   int st = check_shape(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
   st = check_mask(block_mask, mask_head_stride, B, H, N, dtype);
@@ -277,6 +296,7 @@ int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float
                      int64_t N, int64_t d, int dtype, int causal, float scale, float p_drop, uint64_t seed,
                      uint64_t offset, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  if (!all16(q, k, v, o) || !al4(lse)) return ATTN_E_ALIGN;
   int st = check_shape(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
@@ -305,6 +325,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
                      float scale, float p_drop, uint64_t seed, uint64_t offset, void* workspace,
                      size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  if (!all16(q, k, v, o, dout, dq, dk, dv) || !al4(lse)) return ATTN_E_ALIGN;
   int st = check_shape(B, H, N, d, dtype);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_BF16) return ATTN_E_UNSUPPORTED;
@@ -337,6 +358,7 @@ int attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse
                 int64_t Nk, int64_t d, int dtype, int causal, float scale, int num_splits, void* workspace,
                 size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  if (!all16(q, k, v, o) || !al4(lse)) return ATTN_E_ALIGN;
   const int st = check_qk(B, H, Nq, Nk, d, dtype);
   if (st != ATTN_OK) return st;
   if (num_splits < 0 || num_splits > 64) return ATTN_E_SHAPE;
@@ -382,6 +404,7 @@ int attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, cons
                 void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype,
                 int causal, float scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  if (!all16(q, k, v, o, dout, dq, dk, dv) || !al4(lse)) return ATTN_E_ALIGN;
   const int st = check_qk(B, H, Nq, Nk, d, dtype);
   if (st != ATTN_OK) return st;
   if (!isfinite(scale)) return ATTN_E_SCALE;

@@ -30,6 +30,12 @@
  *     inputs and outputs, fp32 accumulation, outputs rounded to nearest-even)
  *     or ATTN_FP32 (fp32 throughout).  N * d must not exceed 2^30 and
  *     B * H * N must stay below 2^31.
+ *   - Alignment: every [B, H, N, d] tensor pointer must be 16-byte aligned
+ *     (the kernels move 16-byte vectors and fetch tiles by 16-byte
+ *     buffer->LDS loads), every float32 [B, H, N] pointer (LSE, D) 4-byte
+ *     aligned, workspaces 256-byte aligned; a block mask may have any
+ *     alignment.  A misaligned pointer returns ATTN_E_ALIGN (a workspace,
+ *     ATTN_E_WORKSPACE) before any HIP call.
  *   - The caller allocates and owns every buffer.  The library allocates no
  *     device memory; scratch memory the backward pass needs is passed in as
  *     `workspace`.
@@ -64,7 +70,9 @@ typedef enum {
   ATTN_E_SCALE = -4,       /* scale is NaN or infinite */
   ATTN_E_WORKSPACE = -5,   /* workspace missing or smaller than required */
   ATTN_E_HIP = -6,         /* a HIP launch failed */
-  ATTN_E_DROPOUT = -7      /* dropout probability outside [0, 1) or NaN */
+  ATTN_E_DROPOUT = -7,     /* dropout probability outside [0, 1) or NaN */
+  ATTN_E_ALIGN = -8        /* a tensor pointer not 16-byte aligned, or an
+                              LSE / D pointer not 4-byte aligned */
 } attn_status;
 
 /*

@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     E, _ = _lib()
-    for st in range(-6, 1):
+    for st in range(-8, 1):
         s = E.attn_status_string(st)
         assert isinstance(s, str) and s and s != "unknown status"
     assert E.attn_status_string(-99) == "unknown status"
@@ -126,6 +126,41 @@ def test_backward_phase_validation():
         assert L.attn_bwd_dq(*ptrs, 1, 1, 16, 64, 0, 1, 0.1, None) == -1
     assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 0, 64, 0, 1, 0.1, None) == -2
     assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 16, 64, 0, 1, float("inf"), None) == -4
+
+
+def test_misaligned_pointers_are_refused():
+    """Tensor pointers must be 16-byte aligned and LSE / D pointers 4-byte
+    aligned (the kernels use 16-byte vector and buffer->LDS accesses): a
+    pointer off by one bf16 element, as a contiguous view at an odd storage
+    offset would give, is refused with ATTN_E_ALIGN (-8) before any HIP call."""
+    _, L = _lib()
+    odd = FAKE + 2  # a valid bf16 address, not 16-byte aligned
+    for i in range(4):  # q, k, v, o
+        ptrs = [FAKE] * 5
+        ptrs[i] = odd
+        assert _fwd(L, ptrs=ptrs) == -8
+    assert _fwd(L, ptrs=[FAKE] * 4 + [FAKE + 2]) == -8  # LSE at 2 bytes
+    for i in range(9):
+        ptrs = [FAKE] * 9
+        ptrs[i] = FAKE + (2 if i != 5 else 1)  # index 5 is LSE
+        assert _bwd(L, ptrs=ptrs) == -8, i
+    assert L.attn_bwd_dsum(FAKE, FAKE, FAKE + 2, 1, 1, 16, 64, 0, None) == -8
+    assert L.attn_bwd_dsum(odd, FAKE, FAKE, 1, 1, 16, 64, 0, None) == -8
+    dk = [FAKE] * 8
+    dk[6] = odd
+    assert L.attn_bwd_dkdv(*dk, 1, 1, 16, 64, 0, 0, 0.1, None) == -8
+    dq = [FAKE] * 7
+    dq[5] = FAKE + 1  # D
+    assert L.attn_bwd_dq(*dq, 1, 1, 16, 64, 0, 1, 0.1, None) == -8
+    bs = [FAKE] * 5
+    bs[2] = odd
+    assert L.attn_fwd_blocksparse(*bs, 1, 1, 300, 64, 0, 0, 0.1, FAKE + 1, 0, None) == -8
+    qk = [FAKE] * 5
+    qk[3] = odd
+    assert L.attn_fwd_qk(*qk, 1, 1, 5, 300, 64, 0, 1, 0.1, 1, None, 0, None) == -8
+    dr = [FAKE] * 5
+    dr[0] = odd
+    assert L.attn_fwd_dropout(*dr, 1, 1, 16, 64, 0, 0, 0.1, 0.1, 1, 0, None) == -8
 
 
 def test_blocksparse_argument_validation():
