@@ -123,9 +123,13 @@ def cpu_baseline(shape, budget_s=12.0, max_heads=256):
         heads += 1
     dt = time.perf_counter() - t0
     threads = 1
+    blas = {}
     for info in threadpool_info():
         if info.get("user_api") == "blas":
             threads = max(threads, int(info.get("num_threads", 1)))
+            blas = {"library": info.get("internal_api"), "version": info.get("version"),
+                    "threads": int(info.get("num_threads", 1)),
+                    "file": os.path.basename(info.get("filepath") or "")}
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -133,6 +137,66 @@ def cpu_baseline(shape, budget_s=12.0, max_heads=256):
         "kind": "oracle",
         "sample": f"{heads} (batch, head) slices of N={n} d={d}, alternating full/causal mask, "
         f"forward + backward in float64 ({dt:.1f} s, {flops / 1e9:.0f} GFLOP by the same convention)",
+        "cpu_model": cpu_model(),
+        "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "blas": blas,
+        "long_context_rows": long_context_rows_baseline(),
+    }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def long_context_rows_baseline():
+    """The oracle's row-restricted forms on the N = 65536 workload (B=1 H=8
+    d=64, causal): O, LSE and dQ of its 512 seeded query rows, and the
+    per-row statistics pass (LSE and D of whole rows, which the key-row
+    gradients need for every row of a head) on one 1024-row block.  Reported
+    as measured rows per second; nothing is extrapolated."""
+    import synth
+    from oracle import attention as A
+
+    w = synth.WORKLOADS["long_n65536_d64_causal"]
+    inp = synth.qkvdo(w.seed, w.shape, w.dtype)
+    bh = w.b * w.h
+    flat = {x: inp[x].reshape(bh, w.n, w.d) for x in ("q", "k", "v", "do")}
+    scale = 1.0 / math.sqrt(w.d)
+    pairs = synth.sample_pairs(w.seed + 1, bh, w.n, 512)
+    t0 = time.perf_counter()
+    for hd in np.unique(pairs[:, 0]):
+        rows = pairs[pairs[:, 0] == hd, 1]
+        a = [flat[x][hd] for x in ("q", "k", "v", "do")]
+        A.forward_rows(a[0], a[1], a[2], rows, True, scale)
+        A.backward_query_rows(a[0], a[1], a[2], a[3], rows, True, scale)
+    t_q = time.perf_counter() - t0
+    # One block of whole rows (the last 256 rows of head 0, the longest
+    # causal rows): LSE, and D_i with dQ (backward_query_rows forms P, dP and
+    # D of its rows), the work the statistics pass does per block plus dQ.
+    a = [flat[x][0] for x in ("q", "k", "v", "do")]
+    rows = np.arange(w.n - 256, w.n)
+    t0 = time.perf_counter()
+    A.forward_rows(a[0], a[1], a[2], rows, True, scale)
+    A.backward_query_rows(a[0], a[1], a[2], a[3], rows, True, scale)
+    t_s = time.perf_counter() - t0
+    return {
+        "workload": "B=1 H=8 N=65536 d=64 causal, float64 oracle",
+        "query_rows": 512,
+        "query_rows_s": round(t_q, 2),
+        "query_rows_per_s": round(512 / t_q, 1),
+        "what": "O, LSE and dQ of the 512 seeded query rows; O, LSE, D and dQ of the last 256 rows of head 0 "
+        "(the per-block work of the statistics pass that the key rows' dK, dV need over every row of a head)",
+        "stat_rows": 256,
+        "stat_rows_s": round(t_s, 2),
+        "stat_rows_per_s": round(256 / t_s, 1),
     }
 
 
@@ -335,6 +399,8 @@ def main():
         "min_hbm_bytes_per_launch": phase_bytes(dph, bh, n, d),
     }
 
+    configs = config_entries(torch, E)
+
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -359,11 +425,60 @@ def main():
         },
         "roofline": roofline,
         "breakdown": breakdown,
+        "configs": configs,
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(shape)
         out["cpu_flash"] = cpu_flash(shape)
     print(json.dumps(out), flush=True)
+
+
+PEAK_FP32_TFLOPS = 157.3
+
+
+def _upload(torch, inp, dtype):
+    if dtype == "bf16":
+        return [torch.from_numpy(inp[x + "_raw"].view(np.int16)).view(torch.bfloat16).cuda()
+                for x in ("q", "k", "v", "do")]
+    return [torch.from_numpy(inp[x + "_raw"]).cuda() for x in ("q", "k", "v", "do")]
+
+
+def config_entries(torch, E, reps=20):
+    """Each measured workload at its own shape, outside the timed step: HIP
+    events on the library's stream around `reps` back-to-back calls of each
+    pass (after 3 warm-up calls); TFLOP/s by the step's convention and as a
+    fraction of the peak of the arithmetic (fp32 vector peak for the float32
+    workload)."""
+    import synth
+
+    out = {}
+    for name in ("fp32_n256_d64", "gpt2s_n1024_d64_causal", "bwd_n2048_d64_causal", "long_n65536_d64_causal"):
+        w = synth.WORKLOADS[name]
+        inp = synth.qkvdo(w.seed, w.shape, w.dtype)
+        q, k, v, do = _upload(torch, inp, w.dtype)
+        del inp
+        scale = 1.0 / math.sqrt(w.d)
+        o, lse = E.attn_fwd(q, k, v, causal=w.causal, scale=scale)
+        ws = torch.empty(E.attn_bwd_workspace_bytes(w.b, w.h, w.n, w.d, E.ATTN_BF16 if w.dtype == "bf16"
+                                                    else E.ATTN_FP32), dtype=torch.uint8, device="cuda")
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+        n_rep = reps if w.n <= 8192 else 3
+        peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+        ff = fwd_flops(w.b * w.h, w.n, w.d, w.causal)
+        t_f = _time_ms(torch, lambda: E.attn_fwd(q, k, v, causal=w.causal, scale=scale, out=o, lse=lse), n_rep, 3)
+        e = {"shape": list(w.shape), "dtype": w.dtype, "mask": "causal" if w.causal else "full",
+             "fwd_ms": round(t_f, 4), "fwd_tflops": round(ff / t_f / 1e9, 2),
+             "fwd_frac_peak": round(ff / t_f / 1e9 / peak, 4),
+             "peak_tflops": peak}
+        if "bwd" in w.passes:
+            t_b = _time_ms(torch, lambda: E.attn_bwd(q, k, v, o, do, lse, causal=w.causal, scale=scale,
+                                                     workspace=ws, grads=grads), n_rep, 3)
+            e.update({"bwd_ms": round(t_b, 4), "bwd_tflops": round(2.5 * ff / t_b / 1e9, 2),
+                      "bwd_frac_peak": round(2.5 * ff / t_b / 1e9 / peak, 4)})
+        out[name] = e
+        del q, k, v, do, o, lse, ws, grads
+        torch.cuda.empty_cache()
+    return out
 
 
 def sweep(torch, E, steps, warmup):

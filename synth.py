@@ -21,6 +21,8 @@ __all__ = [
     "Workload",
     "WORKLOADS",
     "sample_pairs",
+    "peaked_inputs",
+    "ramp_inputs",
 ]
 
 
@@ -113,3 +115,64 @@ def sample_pairs(seed, heads, n, count):
     flat = rng.choice(heads * n, size=count, replace=False)
     flat.sort()
     return np.stack([flat // n, flat % n], axis=1)
+
+
+def ramp_inputs(seed, shape, slope=1.0, height=8.0):
+    """(Q, K, V) of ``shape`` whose scores rise along every row: feature 0 of
+    every query is ``height`` and of key j is ``slope * j`` (rounded to bf16,
+    so equal within runs of a few keys at large j); the other features and V
+    are standard normal.  Returned as in :func:`qkvdo`."""
+    b, h, n, d = shape
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    q[..., 0] = height
+    k[..., 0] = slope * np.arange(n, dtype=np.float32)
+    out = {}
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        bits = f32_to_bf16_bits(x)
+        out[name + "_raw"] = bits
+        out[name] = bf16_bits_to_f32(bits).astype(np.float64)
+    return out
+
+
+def peaked_inputs(seed, shape, product, q_over_k=9.0, do_scale=1.0):
+    """(Q, K, V, dO) of ``shape`` = [B, H, N, d] whose score rows rise toward a
+    chosen key.
+
+    Features 0 and 1 of key j are ``rk * (cos t_j, sin t_j)`` with
+    ``t_j = 2 pi j / N``; those of query i are ``rq * (cos t_p, sin t_p)`` for
+    a key p drawn uniformly per query (every eighth query takes one of the
+    last 64 keys instead), with ``rq * rk = product`` and
+    ``rq / rk = q_over_k``.  Their contribution to the dot product is
+    ``product * cos(t_j - t_p)``, so along a row it climbs toward key p and
+    falls after it.  The other features of Q and K, and V, are standard
+    normal; dO is standard normal times ``do_scale``.  Values are rounded to
+    bf16 and returned as in :func:`qkvdo` (``"<name>"`` float64 values,
+    ``"<name>_raw"`` uint16 bits).
+    """
+    b, h, n, d = shape
+    rq = float(np.sqrt(product * q_over_k))
+    rk = float(np.sqrt(product / q_over_k))
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    do = rng.standard_normal(shape, dtype=np.float32) * np.float32(do_scale)
+    peak = rng.integers(0, n, size=(b, h, n))
+    rows = np.arange(n)
+    late = rows % 8 == 0
+    peak[..., late] = np.maximum(n - 1 - rows[late] % 64, 0)
+    tk = 2.0 * np.pi * np.arange(n) / n
+    tq = 2.0 * np.pi * peak / n
+    k[..., 0] = rk * np.cos(tk)
+    k[..., 1] = rk * np.sin(tk)
+    q[..., 0] = rq * np.cos(tq)
+    q[..., 1] = rq * np.sin(tq)
+    out = {}
+    for name, x in (("q", q), ("k", k), ("v", v), ("do", do)):
+        bits = f32_to_bf16_bits(x)
+        out[name + "_raw"] = bits
+        out[name] = bf16_bits_to_f32(bits).astype(np.float64)
+    return out

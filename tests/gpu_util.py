@@ -56,3 +56,18 @@ def assert_close(gpu, ref, dtype, what=""):
 
 gpu = pytest.mark.gpu
 needs_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+
+
+def oracle_map(fn, items):
+    """Run an oracle function over independent items (usually heads) on the
+    host cores: a thread pool of up to 16 workers, one BLAS thread each
+    (numpy releases the GIL inside its kernels).  Results in item order."""
+    import concurrent.futures
+    import os
+
+    from threadpoolctl import threadpool_limits
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(1):
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            return list(ex.map(fn, items))

@@ -38,3 +38,40 @@ def test_sample_pairs_are_distinct_and_in_range():
     assert len({(int(h), int(r)) for h, r in p}) == 512
     assert p[:, 0].min() >= 0 and p[:, 0].max() < 8
     assert p[:, 1].min() >= 0 and p[:, 1].max() < 65536
+
+
+def _gate_crossings(q, k, scale, causal):
+    """Per (row, 32-key unit): does the unit's max exceed the running max of
+    the earlier units by more than 8 / (scale log2 e), so that one
+    probability taken against the old max exceeds 2^8?"""
+    import math
+
+    n = q.shape[0]
+    s = q @ k.T
+    if causal:
+        s[np.triu_indices(n, 1)] = -np.inf
+    um = s.reshape(n, n // 32, 32).max(-1)
+    prev = np.concatenate([np.full((n, 1), -np.inf), np.maximum.accumulate(um, axis=1)[:, :-1]], axis=1)
+    ok = np.isfinite(um) & np.isfinite(prev)
+    return ((um - prev) * scale * math.log2(math.e) > 8) & ok, ok
+
+
+def test_rescale_inputs_cross_the_gate():
+    """The inputs of tests/test_rescale_gpu.py force the forward's rescale
+    inside rows: the key ramp in every whole unit after a row's first, the peaked
+    rows in at least a tenth of the units and in most rows."""
+    import math
+
+    n = 4096
+    for d in (64, 128):
+        scale = 1.0 / math.sqrt(d)
+        r = synth.ramp_inputs(31 + d, (1, 1, n, d))
+        p = synth.peaked_inputs(41 + d, (1, 1, n, d), 220.0 / scale, do_scale=1.0 / 512)
+        for causal in (False, True):
+            cross, ok = _gate_crossings(r["q"][0, 0], r["k"][0, 0], scale, causal)
+            # (Under the causal mask a row's diagonal unit may hold only a few
+            # keys past the previous unit's max; every whole unit crosses.)
+            whole = 32 * np.arange(n // 32)[None, :] + 31 <= np.arange(n)[:, None] if causal else ok
+            assert cross[ok & whole].all() and (ok & whole).sum() >= ok.sum() - n
+            cross, ok = _gate_crossings(p["q"][0, 0], p["k"][0, 0], scale, causal)
+            assert cross.sum() >= 0.1 * ok.sum() and cross.any(1).sum() >= n // 2
