@@ -114,6 +114,8 @@ def lib():
     L.attn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32, u64,
                                    u64, vp, ctypes.c_size_t, vp]
     L.attn_bwd_dropout.restype = i32
+    L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp]
+    L.attn_bwd_noalloc.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -219,6 +221,32 @@ def attn_bwd(q, k, v, o, do, lse, causal=False, scale=None, workspace=None, grad
     if st != 0:
         raise AttnError(st, "attn_bwd")
     return dq, dk, dv
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # ATTN_NOALLOC_SCRATCH_BYTES in include/attn.h
+
+
+def attn_bwd_noalloc(q, k, v, o, do, lse, grads, causal=False, scale=None):
+    """:func:`attn_bwd` without any allocation: the caller passes the output
+    tensors ``grads = (dq, dk, dv)``, and the library's scratch is a fixed
+    device array (B * H * N <= NOALLOC_SCRATCH_BYTES / 4).  Calls that overlap
+    on one GPU race on that array.  Returns ``grads``."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v), ("o", o), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = grads
+    _check([("dq", dq), ("dk", dk), ("dv", dv)], q.shape, q.dtype, q.device)
+    st = lib().attn_bwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, _dtype_code(q), int(bool(causal)), float(scale),
+        _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_bwd_noalloc")
+    return grads
 
 
 def attn_bwd_dsum(o, do, dsum=None):

@@ -3,8 +3,17 @@
 // returns a status without touching the device.
 #include <math.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "attn_launch.h"
+
+// Scratch memory of attn_bwd_noalloc (D, float32 [B, H, N]): a fixed device
+// array of ATTN_NOALLOC_SCRATCH_BYTES, one copy per GPU, held by the loaded
+// code object until the process ends.  In host code `scratch` names a host
+// stand-in, never the device memory: its device address is looked up per
+// device (scratch_address below) and only that address is used.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -120,6 +129,33 @@ int check_qk(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype)
   return ATTN_OK;
 }
 
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (hipGetSymbolAddress with that device current) and kept.
+constexpr int kMaxDevices = 256;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ATTN_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+// The three backward phases on one stream, D in a.dsum.
+int run_bwd(const attn::BwdArgs& a, bool bf16) {
+  if (attn::bwd_dsum(a, bf16) != hipSuccess) return ATTN_E_HIP;
+  if ((bf16 ? attn::bwd_bf16_dkdv(a) : attn::bwd_f32_dkdv(a)) != hipSuccess) return ATTN_E_HIP;
+  if ((bf16 ? attn::bwd_bf16_dq(a) : attn::bwd_f32_dq(a)) != hipSuccess) return ATTN_E_HIP;
+  return ATTN_OK;
+}
+
 // Dropout arguments: p in [0, 1) (NaN fails the test); the keep threshold
 // and the scale of kept probabilities.
 int check_dropout(float p) { return (p >= 0.f && p < 1.f) ? ATTN_OK : ATTN_E_DROPOUT; }
@@ -150,6 +186,7 @@ const char* attn_status_string(int status) {
     case ATTN_E_HIP: return "HIP kernel launch failed";
     case ATTN_E_DROPOUT: return "dropout probability must lie in [0, 1)";
     case ATTN_E_ALIGN: return "a tensor pointer is not 16-byte aligned (LSE and D: 4-byte)";
+    case ATTN_E_SCRATCH: return "B * H * N float32 values exceed the fixed scratch of attn_bwd_noalloc";
     default: return "unknown status";
   }
 }
@@ -234,11 +271,23 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
     return ATTN_E_WORKSPACE;
   attn::BwdArgs a =
       make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
-  const bool bf16 = dtype == ATTN_BF16;
-  if (attn::bwd_dsum(a, bf16) != hipSuccess) return ATTN_E_HIP;
-  if ((bf16 ? attn::bwd_bf16_dkdv(a) : attn::bwd_f32_dkdv(a)) != hipSuccess) return ATTN_E_HIP;
-  if ((bf16 ? attn::bwd_bf16_dq(a) : attn::bwd_f32_dq(a)) != hipSuccess) return ATTN_E_HIP;
-  return ATTN_OK;
+  return run_bwd(a, dtype == ATTN_BF16);
+}
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                     int dtype, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  if (!all16(q, k, v, o, dout, dq, dk, dv) || !al4(lse)) return ATTN_E_ALIGN;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  if ((size_t)(B * H * N) * sizeof(float) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_E_SCRATCH;
+  void* ws = nullptr;
+  const int sst = scratch_address(&ws);
+  if (sst != ATTN_OK) return sst;
+  attn::BwdArgs a = make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)ws, B, H, N, d, causal, scale, stream);
+  return run_bwd(a, dtype == ATTN_BF16);
 }
 
 int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,

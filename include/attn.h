@@ -71,8 +71,10 @@ typedef enum {
   ATTN_E_WORKSPACE = -5,   /* workspace missing or smaller than required */
   ATTN_E_HIP = -6,         /* a HIP launch failed */
   ATTN_E_DROPOUT = -7,     /* dropout probability outside [0, 1) or NaN */
-  ATTN_E_ALIGN = -8        /* a tensor pointer not 16-byte aligned, or an
+  ATTN_E_ALIGN = -8,       /* a tensor pointer not 16-byte aligned, or an
                               LSE / D pointer not 4-byte aligned */
+  ATTN_E_SCRATCH = -9      /* attn_bwd_noalloc: B * H * N * 4 bytes exceed
+                              ATTN_NOALLOC_SCRATCH_BYTES */
 } attn_status;
 
 /*
@@ -130,6 +132,33 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o,
              int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal,
              float scale, void* workspace, size_t workspace_bytes,
              void* stream);
+
+/*
+ * The backward pass with no allocation and no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * kernels and results as attn_bwd, bit for bit; its scratch (D, float32
+ * [B, H, N]) lives in a fixed device array of ATTN_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.
+ *
+ *   - B * H * N * 4 bytes above ATTN_NOALLOC_SCRATCH_BYTES (B * H * N above
+ *     4194304) return ATTN_E_SCRATCH before any HIP call.
+ *   - The current device must be the device of `stream` and of the tensors.
+ *     The first call on a device looks the array's address up (no
+ *     allocation); a failure there returns ATTN_E_HIP.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap on
+ *     a GPU (two streams, or two host threads) race and must be serialised by
+ *     the caller.  The array's content on entry does not matter (D is fully
+ *     written before it is read).
+ *   - Calls no hipMalloc, hipFree or other allocating routine.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse,
+                     void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int dtype, int causal, float scale,
+                     void* stream);
 
 /*
  * The backward pass in its three phases.  attn_bwd runs them in this order on

@@ -33,6 +33,7 @@ def test_header_declares_the_boundary():
         "attn_bwd_dq",
         "attn_bwd_dropout",
         "attn_bwd_dsum",
+        "attn_bwd_noalloc",
         "attn_bwd_qk",
         "attn_bwd_qk_workspace_bytes",
         "attn_bwd_workspace_bytes",
@@ -54,7 +55,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     E, _ = _lib()
-    for st in range(-8, 1):
+    for st in range(-9, 1):
         s = E.attn_status_string(st)
         assert isinstance(s, str) and s and s != "unknown status"
     assert E.attn_status_string(-99) == "unknown status"
@@ -126,6 +127,30 @@ def test_backward_phase_validation():
         assert L.attn_bwd_dq(*ptrs, 1, 1, 16, 64, 0, 1, 0.1, None) == -1
     assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 0, 64, 0, 1, 0.1, None) == -2
     assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 16, 64, 0, 1, float("inf"), None) == -4
+
+
+def test_noalloc_backward_validation():
+    """attn_bwd_noalloc validates like attn_bwd, and refuses problems whose
+    D (4 * B * H * N bytes) exceeds its fixed scratch, before any HIP call."""
+    E, L = _lib()
+
+    def call(ptrs=(FAKE,) * 9, B=1, H=1, N=16, d=64, dtype=0, scale=0.1):
+        return L.attn_bwd_noalloc(*ptrs, B, H, N, d, dtype, 1, scale, None)
+
+    for i in range(9):
+        ptrs = [FAKE] * 9
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == -1
+    ptrs = [FAKE] * 9
+    ptrs[0] = FAKE + 2
+    assert call(ptrs=ptrs) == -8
+    assert call(d=96) == -3 and call(N=0) == -2 and call(scale=float("nan")) == -4
+    m = re.search(r"#define ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", open(HEADER).read())
+    assert m and int(m.group(1)) << int(m.group(2)) == E.NOALLOC_SCRATCH_BYTES
+    limit = E.NOALLOC_SCRATCH_BYTES // 4  # rows of D
+    assert call(B=1, H=1, N=limit + 1) == -9
+    assert call(B=64, H=1, N=limit // 64 + 1) == -9
+    assert E.attn_status_string(-9) != "unknown status"
 
 
 def test_misaligned_pointers_are_refused():
