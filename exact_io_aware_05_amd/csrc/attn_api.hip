@@ -5,7 +5,7 @@
 
 #include <mutex>
 
-#include "../../include/attn.h"
+#include "attn.h"
 #include "attn_launch.h"
 
 // Scratch memory of attn_bwd_noalloc (D, float32 [B, H, N]): a fixed device

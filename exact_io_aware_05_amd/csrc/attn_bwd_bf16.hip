@@ -969,6 +969,7 @@ hipError_t bwd_bf16_dkdv(const BwdArgs& a) {
   }
   if (a.bmask) return dkdv_t<true, false>(a);
   if (a.nk >= 0) return dkdv_t<false, true>(a);
+  if (a.d == 64) return bwd_bf16_dkdv64(a);
   return dkdv_t<false, false>(a);
 }
 

@@ -102,6 +102,8 @@ hipError_t fwd_f32(const FwdArgs& a);
 // *_dq launchers, `dk`/`dv` only by the *_dkdv launchers.
 hipError_t bwd_dsum(const BwdArgs& a, bool bf16);
 hipError_t bwd_bf16_dkdv(const BwdArgs& a);
+// dK, dV at d = 64 (dense, square lengths, no dropout): single-role waves.
+hipError_t bwd_bf16_dkdv64(const BwdArgs& a);
 hipError_t bwd_bf16_dq(const BwdArgs& a);
 // Query rows per dQ workgroup of the bf16 kernels for head dimension d.
 int bwd_dq_rows(int64_t d);

@@ -108,6 +108,12 @@ def test_long_decode_auto_split():
 @pytest.mark.parametrize("d", [64, 128])
 def test_equal_lengths_match_square_path_bitwise(d, causal):
     # Nq == Nk without a split does the square path's arithmetic in its order.
+    # Exception: at d = 64 the square dense backward computes dK and dV with
+    # the single-role kernel (attn_bwd_kv64.hip), the other paths with the
+    # paired-wave kernel.  The two add the same terms in the same order except
+    # in blocks that take the hi + lo split (a block's lo terms come before its
+    # hi terms in one, after them in the other), so there dK and dV agree to
+    # the bf16 rounding of the outputs.
     E = _api()
     B, H, n = 2, 2, 333
     _announce("qk == square", d, "causal" if causal else "full")
@@ -118,8 +124,12 @@ def test_equal_lengths_match_square_path_bitwise(d, causal):
     o2, l2 = E.attn_fwd(q, k, v, causal=causal)
     g2 = E.attn_bwd(q, k, v, o2, do, l2, causal=causal)
     torch.cuda.synchronize()
-    for a, b in zip((o1, l1) + tuple(g1), (o2, l2) + tuple(g2)):
-        assert torch.equal(a, b)
+    for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), (o1, l1) + tuple(g1), (o2, l2) + tuple(g2)):
+        if d == 64 and name in ("dK", "dV"):
+            diff = (a.float() - b.float()).abs()
+            assert float((diff / b.float().abs().clamp_min(1.0)).max()) <= 2.0**-7, name
+        else:
+            assert torch.equal(a, b), name
 
 
 def _dsum_bytes(B, H, nq):
