@@ -3,8 +3,9 @@
 A step is one pass of the whole hot path over one batch of synthetic bf16
 inputs at B=4, H=16, N=4096, d=128 (the d = 128, N >= 4096 shape the
 performance target is stated for): for the full mask and for the causal mask,
-the forward kernel (O, LSE), then the backward phases D = rowsum(dO * O),
-dK/dV and dQ.  Inputs are resident in HBM before the timed region starts.
+the forward kernel (O, LSE), then the backward as attn_bwd runs it: the dQ
+pass, which also forms D = rowsum(dO * O), then the dK/dV pass.  Inputs are
+resident in HBM before the timed region starts.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        (without --no-cpu the line also carries two CPU references on bounded
@@ -46,13 +47,11 @@ KERNEL_SOURCES = {
     "fwd": "exact_io_aware_05_amd/csrc/attn_fwd_bf16.hip",
     "dkdv": "exact_io_aware_05_amd/csrc/attn_bwd_bf16.hip",
     "dq": "exact_io_aware_05_amd/csrc/attn_bwd_bf16.hip",
-    "dsum": "exact_io_aware_05_amd/csrc/attn_bwd_pre.hip",
 }
 KERNEL_NAMES = {  # substrings of the compiled kernel symbols, as rocprofv3 lists them
     "fwd": "fwd_bf16_kernel",
     "dkdv": "bwd_kv_kernel",
     "dq": "bwd_q_kernel",
-    "dsum": "dsum_kernel",
 }
 
 
@@ -75,7 +74,7 @@ def phase_bytes(phase, bh, n, d):
         "fwd": 4 * t + r,  # read Q, K, V; write O, LSE
         "dsum": 2 * t + r,  # read O, dO; write D
         "dkdv": 6 * t + 2 * r,  # read Q, K, V, dO, LSE, D; write dK, dV
-        "dq": 5 * t + 2 * r,  # read Q, K, V, dO, LSE, D; write dQ
+        "dq": 6 * t + 2 * r,  # read Q, K, V, O, dO, LSE; write dQ, D
     }[phase]
 
 
@@ -255,7 +254,8 @@ class Buffers:
 
 
 def run_step(E, bufs, events=None):
-    """One step: for each mask, forward then the three backward phases."""
+    """One step: for each mask, the forward, then the backward as attn_bwd runs
+    it: dQ with D formed inside the dQ pass, then dK/dV."""
     k = 0
     for B in bufs:
         if events is not None:
@@ -263,19 +263,17 @@ def run_step(E, bufs, events=None):
         E.attn_fwd(B.q, B.k, B.v, B.causal, B.scale, out=B.o, lse=B.lse)
         if events is not None:
             events[k + 1].record()
-        E.attn_bwd_dsum(B.o, B.do, B.dsum)
+        E.attn_bwd_dq_dsum(B.q, B.k, B.v, B.o, B.do, B.lse, B.causal, B.scale, dsum=B.dsum, dq=B.dq)
         if events is not None:
             events[k + 2].record()
         E.attn_bwd_dkdv(B.q, B.k, B.v, B.do, B.lse, B.dsum, B.causal, B.scale, dk=B.dk, dv=B.dv)
         if events is not None:
             events[k + 3].record()
-        E.attn_bwd_dq(B.q, B.k, B.v, B.do, B.lse, B.dsum, B.causal, B.scale, dq=B.dq)
-        if events is not None:
-            events[k + 4].record()
-        k += 5
+        k += 4
 
 
-PHASES = ["fwd", "dsum", "dkdv", "dq"]
+PHASES = ["fwd", "dq", "dkdv"]
+EVENTS_PER_MASK = len(PHASES) + 1
 
 
 def measure(torch, E, shape, steps, warmup):
@@ -283,7 +281,7 @@ def measure(torch, E, shape, steps, warmup):
     for _ in range(warmup):
         run_step(E, bufs)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(10)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * EVENTS_PER_MASK)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
@@ -293,7 +291,7 @@ def measure(torch, E, shape, steps, warmup):
     per = {}
     for mi, mask in enumerate(("full", "causal")):
         for pi, ph in enumerate(PHASES):
-            a = 5 * mi + pi
+            a = EVENTS_PER_MASK * mi + pi
             ms = [ev[s][a].elapsed_time(ev[s][a + 1]) for s in range(steps)]
             per[(mask, ph)] = float(np.mean(ms))
     return (t1 - t0) * 1e3 / steps, per
@@ -368,7 +366,7 @@ def main():
     for mask in ("full", "causal"):
         causal = mask == "causal"
         fwd_ms = per[(mask, "fwd")]
-        bwd_ms = per[(mask, "dsum")] + per[(mask, "dkdv")] + per[(mask, "dq")]
+        bwd_ms = per[(mask, "dq")] + per[(mask, "dkdv")]
         ff = fwd_flops(bh, n, d, causal)
         breakdown[mask] = {
             "fwd_ms": round(fwd_ms, 4),
@@ -495,7 +493,7 @@ def sweep(torch, E, steps, warmup):
                 causal = mask == "causal"
                 ff = fwd_flops(bh, n, d, causal)
                 fwd_ms = per[(mask, "fwd")]
-                bwd_ms = per[(mask, "dsum")] + per[(mask, "dkdv")] + per[(mask, "dq")]
+                bwd_ms = per[(mask, "dq")] + per[(mask, "dkdv")]
                 print(
                     json.dumps(
                         {

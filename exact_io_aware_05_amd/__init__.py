@@ -114,6 +114,8 @@ def lib():
     L.attn_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, f32, u64,
                                    u64, vp, ctypes.c_size_t, vp]
     L.attn_bwd_dropout.restype = i32
+    L.attn_bwd_dq_dsum.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp]
+    L.attn_bwd_dq_dsum.restype = i32
     L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp]
     L.attn_bwd_noalloc.restype = i32
     L.attn_status_string.argtypes = [i32]
@@ -262,6 +264,29 @@ def attn_bwd_dsum(o, do, dsum=None):
     if st != 0:
         raise AttnError(st, "attn_bwd_dsum")
     return dsum
+
+
+def attn_bwd_dq_dsum(q, k, v, o, do, lse, causal=False, scale=None, dsum=None, dq=None):
+    """dQ with D formed inside the dQ pass; returns (dq, dsum), dsum being
+    float32 [B, H, N] (D_i = sum_k dO_ik O_ik) for :func:`attn_bwd_dkdv`."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v), ("o", o), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if dsum is None:
+        dsum = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if dq is None:
+        dq = torch.empty_like(q)
+    _check([("dsum", dsum)], (B, H, N), torch.float32, q.device)
+    _check([("dq", dq)], q.shape, q.dtype, q.device)
+    st = lib().attn_bwd_dq_dsum(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                lse.data_ptr(), dsum.data_ptr(), dq.data_ptr(), B, H, N, d, _dtype_code(q),
+                                int(bool(causal)), float(scale), _stream_ptr(q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_dq_dsum")
+    return dq, dsum
 
 
 def attn_bwd_dkdv(q, k, v, do, lse, dsum, causal=False, scale=None, dk=None, dv=None):

@@ -148,11 +148,19 @@ int scratch_address(void** out) {
   return ATTN_OK;
 }
 
-// The three backward phases on one stream, D in a.dsum.
-int run_bwd(const attn::BwdArgs& a, bool bf16) {
-  if (attn::bwd_dsum(a, bf16) != hipSuccess) return ATTN_E_HIP;
-  if ((bf16 ? attn::bwd_bf16_dkdv(a) : attn::bwd_f32_dkdv(a)) != hipSuccess) return ATTN_E_HIP;
-  if ((bf16 ? attn::bwd_bf16_dq(a) : attn::bwd_f32_dq(a)) != hipSuccess) return ATTN_E_HIP;
+// The backward phases on one stream, D in a.dsum.  bf16: the dQ pass forms
+// D (from O and dO) and writes it, then dK/dV reads it; fp32: D first, then
+// dK/dV, then dQ.
+int run_bwd(attn::BwdArgs a, bool bf16) {
+  if (bf16) {
+    a.dq_forms_dsum = true;
+    if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;
+    if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
+    return ATTN_OK;
+  }
+  if (attn::bwd_dsum(a, false) != hipSuccess) return ATTN_E_HIP;
+  if (attn::bwd_f32_dkdv(a) != hipSuccess) return ATTN_E_HIP;
+  if (attn::bwd_f32_dq(a) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
 }
 
@@ -258,6 +266,23 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, c
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
+int attn_bwd_dq_dsum(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, float* dsum, void* dq, int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                     int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dsum || !dq) return ATTN_E_NULL;
+  if (!all16(q, k, v, o, dout, dq) || !al4(lse) || !al4(dsum)) return ATTN_E_ALIGN;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  attn::BwdArgs a = make_bwd(q, k, v, o, dout, lse, dq, nullptr, nullptr, dsum, B, H, N, d, causal, scale, stream);
+  if (dtype == ATTN_BF16) {
+    a.dq_forms_dsum = true;
+    return attn::bwd_bf16_dq(a) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+  }
+  if (attn::bwd_dsum(a, false) != hipSuccess) return ATTN_E_HIP;
+  return attn::bwd_f32_dq(a) == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal,
              float scale, void* workspace, size_t workspace_bytes, void* stream) {
@@ -335,10 +360,7 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
       make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
   a.bmask = block_mask;
   a.mask_stride = mask_head_stride;
-  if (attn::bwd_dsum(a, true) != hipSuccess) return ATTN_E_HIP;
-  if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
-  if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;
-  return ATTN_OK;
+  return run_bwd(a, true);
 }
 
 int attn_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
@@ -388,10 +410,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
       make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
   a.dropout = true;
   a.drop = make_drop(p_drop, seed, offset);
-  if (attn::bwd_dsum(a, true) != hipSuccess) return ATTN_E_HIP;
-  if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
-  if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;
-  return ATTN_OK;
+  return run_bwd(a, true);
 }
 
 size_t attn_fwd_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype,
@@ -469,6 +488,9 @@ int attn_bwd_qk(const void* q, const void* k, const void* v, const void* o, cons
     a.kchunk = sp.kchunk;
     a.dqpart = (float*)((char*)workspace + align256((size_t)(B * H * Nq) * sizeof(float)));
   }
+  // Without a dQ split the dQ pass forms D, as in attn_bwd; with one, each
+  // chunk's workgroups would form it again, so D comes first.
+  if (sp.nsplit <= 1) return run_bwd(a, true);
   if (attn::bwd_dsum(a, true) != hipSuccess) return ATTN_E_HIP;
   if (attn::bwd_bf16_dkdv(a) != hipSuccess) return ATTN_E_HIP;
   if (attn::bwd_bf16_dq(a) != hipSuccess) return ATTN_E_HIP;

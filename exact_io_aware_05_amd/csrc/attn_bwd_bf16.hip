@@ -600,7 +600,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
                                                            float scale, float sl2e,
                                                            const uint8_t* __restrict__ bmask, long long mask_stride,
                                                            int nb, int nk_arg, int coff_arg, DropArgs dr,
-                                                           int kchunk, float* __restrict__ dqpart) {
+                                                           int kchunk, float* __restrict__ dqpart,
+                                                           const uint16_t* __restrict__ Osrc,
+                                                           float* __restrict__ Dout) {
   constexpr int BR = NW * 32, BC = 64;
 
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[BC * D];
@@ -660,7 +662,30 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
     gf[s] = as_bf16x8(bload16(rdo, (uint32_t)qrow * (D * 2) + 32 * s + 16 * hh));
   }
   const float l2 = qrow < n ? LSE[(size_t)bh * n + qrow] * kLog2e : 0.f;
-  const float dq_d = qrow < n ? Dsum[(size_t)bh * n + qrow] : 0.f;
+  // D_i = dO_i . O_i: read from Dsum, or (Osrc given) formed here from the
+  // row's O, whose fragments are loaded like dO's (this lane: half hh of the
+  // row's features), summed over the two lane halves, and written to Dout
+  // for the key-stationary pass, which then runs after this one.  Rows past
+  // n load as zero.
+  float dq_d;
+  if (Osrc != nullptr) {
+    const auto ro = make_rsrc(Osrc + head, head_bytes);
+    float part = 0.f;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4 ov = bload16(ro, (uint32_t)qrow * (D * 2) + 32 * s + 16 * hh);
+      const u32x4 gv = __builtin_bit_cast(u32x4, gf[s]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        part = fmaf(__uint_as_float(ov[i] << 16), __uint_as_float(gv[i] << 16), part);
+        part = fmaf(__uint_as_float(ov[i] & 0xFFFF0000u), __uint_as_float(gv[i] & 0xFFFF0000u), part);
+      }
+    }
+    dq_d = half_sum(part);
+    if (hh == 0 && qrow < n) Dout[(size_t)bh * n + qrow] = dq_d;
+  } else {
+    dq_d = qrow < n ? Dsum[(size_t)bh * n + qrow] : 0.f;
+  }
 
   f32x16 dqa[D / 32];
 #pragma unroll
@@ -935,11 +960,14 @@ hipError_t launch_dq(const BwdArgs& a) {
   const int nb = (n + kSparseBlock - 1) / kSparseBlock;
   const int nk = QK ? (int)a.nk : n;
   const bool split = QK && a.nsplit > 1;
+  const bool form_d = a.dq_forms_dsum && !split;
   hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK, DROP>), dim3(total * (split ? a.nsplit : 1)),
                      dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (const uint16_t*)a.dout, a.lse, a.dsum, (uint16_t*)a.dq, n, nqb, total, a.scale,
+                     (const uint16_t*)a.dout, a.lse, form_d ? nullptr : a.dsum, (uint16_t*)a.dq, n, nqb, total,
+                     a.scale,
                      a.scale * kLog2e, a.bmask, (long long)a.mask_stride, nb, nk, nk - n, a.drop,
-                     split ? a.kchunk : 0, split ? a.dqpart : nullptr);
+                     split ? a.kchunk : 0, split ? a.dqpart : nullptr,
+                     form_d ? (const uint16_t*)a.o : nullptr, form_d ? a.dsum : nullptr);
   if (!split) return hipGetLastError();
   const long long n4 = a.bh * a.n * (long long)D / 4;
   const long long blocks = std::min<long long>((n4 + 255) / 256, 4096);

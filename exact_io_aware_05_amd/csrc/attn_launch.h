@@ -89,6 +89,10 @@ struct BwdArgs {
   int nsplit = 1;
   int kchunk = 0;
   float* dqpart = nullptr;
+  // bf16 dQ launchers (no dQ split): form D from `o` and `dout` inside the
+  // dQ kernel and write it to `dsum`, instead of reading it from there; the
+  // dK/dV launch then follows the dQ launch.
+  bool dq_forms_dsum = false;
 };
 
 // Block size of the block-sparse mask (query and key rows per block).

@@ -161,10 +161,10 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v,
                      void* stream);
 
 /*
- * The backward pass in its three phases.  attn_bwd runs them in this order on
- * one stream; they are exposed so that the two gradient phases, which are
- * independent once D is known, can run on two streams, and so that each
- * phase can be timed on its own.  Arguments mean what they mean for attn_bwd;
+ * The backward pass in its three phases.  They are exposed so that the two
+ * gradient phases, which are independent once D is known, can run on two
+ * streams, and so that each phase can be timed on its own (attn_bwd itself
+ * runs attn_bwd_dq_dsum, below, then attn_bwd_dkdv for bf16).  Arguments mean what they mean for attn_bwd;
  * `dsum` is float32 [B, H, N] device memory (D_i = sum_k dO_ik O_ik), written
  * by attn_bwd_dsum and read by the other two.  Same validation and error
  * behaviour as attn_bwd (a NULL dsum is ATTN_E_NULL).
@@ -181,6 +181,19 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
                 const float* lse, const float* dsum, void* dq, int64_t B,
                 int64_t H, int64_t N, int64_t d, int dtype, int causal,
                 float scale, void* stream);
+
+/*
+ * The dQ phase with D formed inside it: reads O and dO, writes
+ * dsum (D_i = sum_k dO_ik O_ik, float32 [B, H, N]) and dq.  attn_bwd runs
+ * this, then attn_bwd_dkdv, for bf16 (one pass fewer over O and dO than
+ * attn_bwd_dsum followed by attn_bwd_dq); for fp32 it runs attn_bwd_dsum and
+ * attn_bwd_dq.  Same validation and error behaviour as attn_bwd_dq.
+ */
+int attn_bwd_dq_dsum(const void* q, const void* k, const void* v,
+                     const void* o, const void* dout, const float* lse,
+                     float* dsum, void* dq, int64_t B, int64_t H, int64_t N,
+                     int64_t d, int dtype, int causal, float scale,
+                     void* stream);
 
 /*
  * Block-sparse attention: the block-sparse variant of the method that the

@@ -31,6 +31,7 @@ def test_header_declares_the_boundary():
         "attn_bwd_blocksparse",
         "attn_bwd_dkdv",
         "attn_bwd_dq",
+        "attn_bwd_dq_dsum",
         "attn_bwd_dropout",
         "attn_bwd_dsum",
         "attn_bwd_noalloc",
@@ -127,6 +128,25 @@ def test_backward_phase_validation():
         assert L.attn_bwd_dq(*ptrs, 1, 1, 16, 64, 0, 1, 0.1, None) == -1
     assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 0, 64, 0, 1, 0.1, None) == -2
     assert L.attn_bwd_dq(*([FAKE] * 7), 1, 1, 16, 64, 0, 1, float("inf"), None) == -4
+
+
+def test_dq_dsum_validation():
+    _, L = _lib()
+
+    def call(ptrs=(FAKE,) * 8, N=16, d=64, dtype=0, scale=0.1):
+        return L.attn_bwd_dq_dsum(*ptrs, 1, 2, N, d, dtype, 1, scale, None)
+
+    for i in range(8):
+        ptrs = [FAKE] * 8
+        ptrs[i] = None
+        assert call(ptrs=ptrs) == -1
+    ptrs = [FAKE] * 8
+    ptrs[6] = FAKE + 2  # dsum: 4-byte alignment
+    assert call(ptrs=ptrs) == -8
+    ptrs = [FAKE] * 8
+    ptrs[3] = FAKE + 2  # o
+    assert call(ptrs=ptrs) == -8
+    assert call(d=32) == -3 and call(N=0) == -2 and call(scale=float("inf")) == -4
 
 
 def test_noalloc_backward_validation():
