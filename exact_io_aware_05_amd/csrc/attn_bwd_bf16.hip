@@ -144,445 +144,462 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   const int grp = w & 3;        // key group: keys 32*grp .. +31 of the block
   const bool s_role = w < 4;    // S wave (dV) or dP wave (dK)
 
-  // Causal: low key blocks see the most queries; they come first.
+  // Key blocks: under the causal mask (square lengths, no block mask or
+  // dropout) a workgroup takes key block j and then its mirror nkb - 1 - j,
+  // so every workgroup visits the same number of query tiles (block kb
+  // visits ntq - 2 kb of them) and there are half as many workgroup
+  // hand-overs; otherwise one block, low key blocks (the most queries under
+  // the causal mask) first.
+  constexpr bool PAIRED = CAUSAL && !SPARSE && !QK && !DROP;
   const int lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / nkb, kb = lid % nkb;
-  const int k0 = kb * BKV;
-  const int kw0 = k0 + 32 * grp;
-  const int key = kw0 + l32;
-  // Unequal lengths (QK): n is the query length, nk the key length, and
-  // query i sees key j when j <= i + coff (causal, bottom-right).
-  const int nk = QK ? nk_arg : n;
-  const int coff = (QK && CAUSAL) ? coff_arg : 0;
-
-  const size_t head = (size_t)bh * (size_t)n * D;
-  const size_t khead = (size_t)bh * (size_t)nk * D;
-  const uint32_t head_bytes = (uint32_t)n * D * 2u;
-  // Q and dO tiles are fetched through inline asm (dma_tile_asm): the
-  // compiler would otherwise make LDS accesses of one buffer wait for the
-  // fetch in flight into another; the waits it needs are explicit here.
-  const RsrcWords rq = rsrc_words(Q + head, head_bytes);
-  const RsrcWords rdo = rsrc_words(dO + head, head_bytes);
-  const RsrcWords rl = rsrc_words(LSE + (size_t)bh * n, (uint32_t)n * 4u);
-  const RsrcWords rd = rsrc_words(Dsum + (size_t)bh * n, (uint32_t)n * 4u);
-
-  // B operands of S (K rows) for the S wave, of dP (V rows) for the dP wave.
-  bf16x8 bf[D / 16];
-  {
-    const auto rkv = make_rsrc((s_role ? K : V) + khead, (uint32_t)nk * D * 2u);
+  const int nper = PAIRED ? (nkb + 1) / 2 : nkb;
+  const int bh = lid / nper, kj = lid % nper;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) bf[s] = as_bf16x8(bload16(rkv, (uint32_t)key * (D * 2) + 32 * s + 16 * hh));
-    // Complete before any tile fetch is issued: a wait for these registers
-    // inside the tile loop would also wait for the fetches in flight.
-    wait_vmem();
-  }
-
-  f32x16 acc[D / 32];  // dV^T (S wave) or dK^T (dP wave)
-#pragma unroll
-  for (int e = 0; e < D / 32; ++e)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[e][r] = 0.f;
-
-  const int ntq = (n + BQ - 1) / BQ;
-  const int it0 = CAUSAL ? max(0, k0 - coff) / BQ : 0;
-  // A tile whose queries all precede this key group is skipped (causal);
-  // both waves of a pair decide alike.
-  auto active = [&](int i) ATTN_INLINE { return !CAUSAL || (i * BQ + BQ - 1 >= kw0 - coff); };
-
-  // Block-sparse: the query tiles whose mask block (a 64-row tile is half of
-  // a 128-row block) may attend this key block (a workgroup's 128 keys are
-  // one mask block column), listed in LDS in increasing order.
-  uint32_t* const tlist = reinterpret_cast<uint32_t*>(smem + SMALL + 6 * TB + PXB);
-  int* const tcount = reinterpret_cast<int*>(tlist + kMaxSparseTiles);
-  int tcnt = 0;
-  if constexpr (SPARSE) {
-    const uint8_t* mcol = bmask + (size_t)bh * mask_stride + kb;
-    const int nbq = (n + kSparseBlock - 1) / kSparseBlock;
-    tcnt = build_tile_list([&](int i) ATTN_INLINE { return mcol[(size_t)(i >> 1) * nbq] != 0; }, it0, ntq, tlist,
-                           tcount, w, lane);
-  }
-
-  // Query rows past n load as zero (Q, dO, LSE, D), so they contribute
-  // nothing: P = 1 is finite and multiplies dO = 0 and dS = 0.
-  // A tile's batch of fetches: LSE and D rows (wave 0, one load each), then
-  // the Q and dO tiles (2 * IPW loads per wave).  Every tile issues the same
-  // batch (past the last tile: copies of the last one, never read), so the
-  // counts below hold on every path.
-  constexpr int SMALLN = 2;  // LSE and D loads of wave 0
-  auto dma = [&](int i, auto b) ATTN_INLINE {
-    if (w == 0) {
-      const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)i * (BQ * 4));
-      const uint32_t sbase = (uint32_t)(uintptr_t)(ATTN_LDS char*)smem;
-      dma_row64_asm(rl, sbase + 512u * decltype(b)::value, off, lane);
-      dma_row64_asm(rd, sbase + 512u * decltype(b)::value + 256u, off, lane);
+  for (int rep = 0; rep < (PAIRED ? 2 : 1); ++rep) {
+    const int kb = rep == 0 ? kj : nkb - 1 - kj;
+    if (rep == 1) {
+      if (kb == kj) break;
+      // Every read of the first block's tiles and P exchange is done before
+      // the second block's fetches refill the buffers.
+      __syncthreads();
     }
-    dma_tile_asm<D, NW>(rq, q_at(b), i * BQ, w, lane);
-    dma_tile_asm<D, NW>(rdo, g_at(b), i * BQ, w, lane);
-  };
-  // Wave 0 scales the landed LSE row of buffer b to base 2 and negates the
-  // D row, in place; the tiles fetched after them (LATER loads) may still be
-  // in flight.
-  auto fix_small = [&](auto b, auto later) ATTN_INLINE {
-    if (w == 0) {
-      wait_vmem_upto<decltype(later)::value>();
-      asm volatile("" ::: "memory");
-      lse_at(b)[lane] *= kLog2e;
-      dsm_at(b)[lane] = -dsm_at(b)[lane];
-    }
-  };
-  // End of a tile: the batch of the next tile must have landed; the batch
-  // of the tile after it (issued last) stays in flight.
-  auto handover = [&]() ATTN_INLINE {
-    if (w == 0)
-      wait_vmem_upto<SMALLN + 2 * IPW>();
-    else
-      wait_vmem_upto<2 * IPW>();
-    barrier_lds();
-  };
+    const int k0 = kb * BKV;
+    const int kw0 = k0 + 32 * grp;
+    const int key = kw0 + l32;
+    // Unequal lengths (QK): n is the query length, nk the key length, and
+    // query i sees key j when j <= i + coff (causal, bottom-right).
+    const int nk = QK ? nk_arg : n;
+    const int coff = (QK && CAUSAL) ? coff_arg : 0;
 
-  float* px = pxs + grp * (2 * 4 * 64 * 4);
+    const size_t head = (size_t)bh * (size_t)n * D;
+    const size_t khead = (size_t)bh * (size_t)nk * D;
+    const uint32_t head_bytes = (uint32_t)n * D * 2u;
+    // Q and dO tiles are fetched through inline asm (dma_tile_asm): the
+    // compiler would otherwise make LDS accesses of one buffer wait for the
+    // fetch in flight into another; the waits it needs are explicit here.
+    const RsrcWords rq = rsrc_words(Q + head, head_bytes);
+    const RsrcWords rdo = rsrc_words(dO + head, head_bytes);
+    const RsrcWords rl = rsrc_words(LSE + (size_t)bh * n, (uint32_t)n * 4u);
+    const RsrcWords rd = rsrc_words(Dsum + (size_t)bh * n, (uint32_t)n * 4u);
 
-  // Dropout keep bits of this lane's key for queries qbase + 0..3 (bit k).
-  // One generator call covers four consecutive keys of one query, so the
-  // four lanes of a quad (keys 4a .. 4a + 3) call it for the four queries
-  // and exchange words by a 4 x 4 transpose within the quad (DPP rotations).
-  auto quad_keep = [&](int qbase) ATTN_INLINE -> uint32_t {
-    const int tq = lane & 3;
-    const u32x4 wd = philox4x32_10((uint32_t)(kw0 + (l32 & ~3)) >> 2, (uint32_t)(qbase + tq), (uint32_t)bh,
-                                   dr.offset, dr.seed_lo, dr.seed_hi);
-    // y[k] = word tq of quad lane k: query qbase + k, this lane's key.
-    uint32_t y[4];
-    auto pick = [&](int idx) ATTN_INLINE {
-      return idx == 0 ? wd[0] : idx == 1 ? wd[1] : idx == 2 ? wd[2] : wd[3];
-    };
+    // B operands of S (K rows) for the S wave, of dP (V rows) for the dP wave.
+    bf16x8 bf[D / 16];
+    {
+      const auto rkv = make_rsrc((s_role ? K : V) + khead, (uint32_t)nk * D * 2u);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) y[k] = 0u;
-    y[0] = tq == 0 ? wd[0] : y[0];
-    y[1] = tq == 1 ? wd[1] : y[1];
-    y[2] = tq == 2 ? wd[2] : y[2];
-    y[3] = tq == 3 ? wd[3] : y[3];
-    auto rot = [&](auto rc) ATTN_INLINE {
-      constexpr int RT = decltype(rc)::value;
-      // Lane s sends its word (s - RT) mod 4; lane r receives from lane
-      // (r + RT) mod 4 its word r.
-      const uint32_t x = pick((tq - RT) & 3);
-      constexpr int ctrl = ((0 + RT) & 3) | (((1 + RT) & 3) << 2) | (((2 + RT) & 3) << 4) | (((3 + RT) & 3) << 6);
-      const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, 0xF, 0xF, false);
-      const int src = (tq + RT) & 3;
-      y[0] = src == 0 ? r : y[0];
-      y[1] = src == 1 ? r : y[1];
-      y[2] = src == 2 ? r : y[2];
-      y[3] = src == 3 ? r : y[3];
-    };
-    rot(int_c<1>{});
-    rot(int_c<2>{});
-    rot(int_c<3>{});
-    uint32_t bits = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) bits |= (y[k] >= dr.thr ? 1u : 0u) << k;
-    return bits;
-  };
+      for (int s = 0; s < D / 16; ++s) bf[s] = as_bf16x8(bload16(rkv, (uint32_t)key * (D * 2) + 32 * s + 16 * hh));
+      // Complete before any tile fetch is issued: a wait for these registers
+      // inside the tile loop would also wait for the fetches in flight.
+      wait_vmem();
+    }
 
-  // Products of P or dS for one half tile into dV or dK.  Where the half
-  // tile holds a weight (P, or scale * dS) >= 1/16 the values enter as hi +
-  // lo bf16 pairs (a
-  // single bf16 rounding, relative 2^-9, of a probability near 1 can move a
-  // column sum of magnitude > 4 by more than the output's own rounding
-  // leaves); each term is one call, with packed operands h[u].
-  auto acc_plain = [&](auto& tr, const uint16_t* bs, const bf16x8* h, int t) ATTN_INLINE {
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 a[2][D / 32];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) a[u][e] = tr.cols(bs, 32 * t + 16 * u, e);
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[0][e], h[0], acc[e]);
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[1][e], h[1], acc[e]);
-    pipeline_reads2<D / 16>();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // The products of both half tiles (operands h0 for queries 0-31, h1 for
-  // 32-63) as one stream of 4 D / 16 MFMAs, so that operand reads run ahead
-  // across the two halves instead of stalling at the start of each.
-  auto acc_pair = [&](auto& tr, const uint16_t* bs, const bf16x8* h0, const bf16x8* h1) ATTN_INLINE {
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 a[4][D / 32];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) a[q][e] = tr.cols(bs, 16 * q, e);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bf16x8& hq = q < 2 ? h0[q & 1] : h1[q & 1];
-#pragma unroll
-      for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[q][e], hq, acc[e]);
-    }
-    pipeline_reads2<D / 8, 4>();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // Wave-uniform test for the split.  P enters dV as it is; dS enters dK
-  // unscaled (the scale is applied to the accumulator at the end), so its
-  // threshold is divided by |scale|: a term's rounding error in the output
-  // is then bounded alike in both products.
-  const float tau = s_role ? kSplitThreshold : kSplitThreshold / fabsf(scale);
-  auto needs_split = [&](const float* vt) ATTN_INLINE {
-    float vmax = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, fabsf(vt[r]));
-    return __builtin_amdgcn_ballot_w64(vmax >= tau) != 0;
-  };
-  // Two independent MFMA chains (queries 0-31 and 32-63 of the tile) over
-  // the row-major tile `src`, with this wave's key-side fragments.
-  auto chains = [&](auto& tr, const uint16_t* src, f32x16& c0, f32x16& c1) ATTN_INLINE {
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 a0[D / 16], a1[D / 16];
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      a0[s] = tr.rows(src, 0, s);
-      a1[s] = tr.rows(src, 32, s);
-    }
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) {
-      c0 = mfma32(a0[s], bf[s], c0);
-      c1 = mfma32(a1[s], bf[s], c1);
-    }
-    pipeline_reads<D / 8>();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // Tile loop skeleton shared by both roles (same barriers in both): tile i
-  // lives in buffer b = (i - it0) mod 3.  body(b, i, mid) does the role's
-  // work on tile i and calls mid() exactly once, between its two halves.
-  auto run_dense = [&](auto&& body) ATTN_INLINE {
-    auto step = [&](auto b, int i) ATTN_INLINE {
-      constexpr int B = decltype(b)::value;
-      body(b, i, [&]() ATTN_INLINE {
-        fix_small(int_c<(B + 1) % 3>{}, int_c<2 * IPW>{});  // LSE of tile i + 1
-        barrier_lds();  // P of tile i is published; reads of tile i - 1 are done
-        dma(min(i + 2, ntq - 1), int_c<(B + 2) % 3>{});
-      });
-      handover();
-    };
-    dma(it0, int_c<0>{});
-    dma(min(it0 + 1, ntq - 1), int_c<1>{});
-    fix_small(int_c<0>{}, int_c<SMALLN + 4 * IPW>{});
-    handover();
-    for (int it = it0; it < ntq; it += 3) {
-      step(int_c<0>{}, it);
-      if (it + 1 >= ntq) break;
-      step(int_c<1>{}, it + 1);
-      if (it + 2 >= ntq) break;
-      step(int_c<2>{}, it + 2);
-    }
-  };
-  // The same sequence over the listed tiles: position p holds tile T(p) in
-  // buffer p mod 3.
-  auto run_list = [&](auto&& body) ATTN_INLINE {
-    auto T = [&](int p) ATTN_INLINE { return __builtin_amdgcn_readfirstlane((int)tlist[p]); };
-    auto step = [&](auto b, int p) ATTN_INLINE {
-      constexpr int B = decltype(b)::value;
-      body(b, T(p), [&]() ATTN_INLINE {
-        fix_small(int_c<(B + 1) % 3>{}, int_c<2 * IPW>{});  // LSE of the next tile
-        barrier_lds();  // P of this tile is published; reads of the previous one are done
-        dma(T(min(p + 2, tcnt - 1)), int_c<(B + 2) % 3>{});
-      });
-      handover();
-    };
-    if (tcnt == 0) return;
-    dma(T(0), int_c<0>{});
-    dma(T(min(1, tcnt - 1)), int_c<1>{});
-    fix_small(int_c<0>{}, int_c<SMALLN + 4 * IPW>{});
-    handover();
-    for (int p = 0; p < tcnt; p += 3) {
-      step(int_c<0>{}, p);
-      if (p + 1 >= tcnt) break;
-      step(int_c<1>{}, p + 1);
-      if (p + 2 >= tcnt) break;
-      step(int_c<2>{}, p + 2);
-    }
-  };
-  auto run = [&](auto&& body) ATTN_INLINE {
-    if constexpr (SPARSE)
-      run_list(body);
-    else
-      run_dense(body);
-    wait_vmem();  // no fetch outlives the loop
-  };
-
-  if (s_role) {
-    // S wave: S = Q K^T, P = exp(S - LSE) published through LDS, then
-    // dV^T += dO^T P.
-    const TileReader<D, 0, GSHIFT> TR(lane);
-    run([&](auto b, int i, auto&& mid) ATTN_INLINE {
-      const bool act = active(i);
-      float v[2][16];
-      if (act) {
-        const float* lse2s = lse_at(b);
-        f32x16 c0, c1;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          c0[r] = 0.f;
-          c1[r] = 0.f;
-        }
-        chains(TR, q_at(b), c0, c1);
-        // Exponent arguments; on the diagonal tiles only (a wave-uniform
-        // branch), entries whose key follows the query become -inf, whose
-        // exp2 is 0.  Written as selects inside the exponential loop, the
-        // mask ran on every tile.
-        float x[2][16];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * t + 8 * g + 4 * hh]);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) x[t][4 * g + k] = fmaf(t == 0 ? c0[4 * g + k] : c1[4 * g + k], sl2e, -l4[k]);
-          }
-        if (CAUSAL && i * BQ < kw0 + 31 - coff) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int q = i * BQ + 32 * t + crow(r, hh);
-              x[t][r] = key > q + coff ? -INFINITY : x[t][r];
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int qbase = i * BQ + 32 * t + 8 * g + 4 * hh;  // queries qbase + k of registers 4g + k
-            uint32_t keep = 0xFu;
-            if constexpr (DROP) keep = quad_keep(qbase);
-            f32x4 o;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              const float pv = fast_exp2(x[t][4 * g + k]);
-              if constexpr (DROP) {
-                // dV takes the dropped, rescaled probability; the dP wave
-                // gets P with the keep bit in the sign (P >= 0).
-                const bool kept = (keep >> k) & 1u;
-                v[t][4 * g + k] = kept ? pv * dr.keep_scale : 0.f;
-                o[k] = kept ? pv : -pv;
-              } else {
-                v[t][4 * g + k] = pv;
-                o[k] = pv;
-              }
-            }
-            *reinterpret_cast<f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]) = o;
-          }
-      }
-      mid();
-      if (act) {
-        // hi terms always (both halves as one stream), lo terms only where
-        // the half tile needs them: the accumulators are only ever updated in
-        // place (no alternative paths that the register allocator would join
-        // with copies).
-        const bf16x8 h0[2] = {pack_bf16x8(v[0]), pack_bf16x8(v[0] + 8)};
-        const bf16x8 h1[2] = {pack_bf16x8(v[1]), pack_bf16x8(v[1] + 8)};
-        const bool sp0 = needs_split(v[0]), sp1 = needs_split(v[1]);
-        acc_pair(TR, g_at(b), h0, h1);
-        if (sp0) {
-          const bf16x8 l[2] = {split_lo_bf16x8(v[0], h0[0]), split_lo_bf16x8(v[0] + 8, h0[1])};
-          acc_plain(TR, g_at(b), l, 0);
-        }
-        if (sp1) {
-          const bf16x8 l[2] = {split_lo_bf16x8(v[1], h1[0]), split_lo_bf16x8(v[1] + 8, h1[1])};
-          acc_plain(TR, g_at(b), l, 1);
-        }
-      }
-    });
-  } else {
-    // dP wave: dP = dO V^T accumulated onto -D (registers run over queries),
-    // so it ends with dP - D; after P arrives, dS = P * (dP - D).  The dK^T
-    // += Q^T dS products of each half tile are deferred to the next tile's
-    // first half, with dS kept packed in registers (hi and, where the half
-    // tile needs the split, lo bf16 terms).
-    const TileReader<D, GSHIFT, 0> TR(lane);
-    bf16x8 dhi[2][2], dlo[2][2];
-    bool pend = false, spl0 = false, spl1 = false;
-    auto deferred = [&](const uint16_t* qs) ATTN_INLINE {
-      acc_pair(TR, qs, dhi[0], dhi[1]);
-      if (spl0) acc_plain(TR, qs, dlo[0], 0);
-      if (spl1) acc_plain(TR, qs, dlo[1], 1);
-    };
-    run([&](auto b, int i, auto&& mid) ATTN_INLINE {
-      constexpr int BP = (decltype(b)::value + 2) % 3;  // buffer of the previous tile
-      const bool act = active(i);
-      // The accumulators start from -D (with dropout from 0: dP is needed
-      // alone, dS = P (Z dP / (1 - p) - D)).  The -D rows are read before
-      // the deferred products, which hide the LDS latency; read just before
-      // the chains, the first product waited for them.
-      f32x16 c0, c1;
-      {
-        const float* dsms = dsm_at(b);
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dsms[8 * g + 4 * hh]);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dsms[32 + 8 * g + 4 * hh]);
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            c0[4 * g + k] = DROP ? 0.f : d0[k];
-            c1[4 * g + k] = DROP ? 0.f : d1[k];
-          }
-        }
-      }
-      if (pend) deferred(q_at(int_c<BP>{}));
-      if (act) chains(TR, g_at(b), c0, c1);
-      mid();
-      pend = act;
-      if (act) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float v[16];
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 p4 = *reinterpret_cast<const f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]);
-            if constexpr (DROP) {
-              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsm_at(b)[32 * t + 8 * g + 4 * hh]);
-#pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                const float dpv = t == 0 ? c0[4 * g + k] : c1[4 * g + k];
-                const bool kept = (__float_as_uint(p4[k]) >> 31) == 0u;
-                v[4 * g + k] = fabsf(p4[k]) * ((kept ? dpv * dr.keep_scale : 0.f) + d4[k]);  // d4 = -D
-              }
-            } else {
-#pragma unroll
-              for (int k = 0; k < 4; ++k) v[4 * g + k] = (t == 0 ? c0[4 * g + k] : c1[4 * g + k]) * p4[k];
-            }
-          }
-          const bool sp = needs_split(v);
-          (t == 0 ? spl0 : spl1) = sp;
-          dhi[t][0] = pack_bf16x8(v);
-          dhi[t][1] = pack_bf16x8(v + 8);
-          if (sp) {
-            dlo[t][0] = split_lo_bf16x8(v, dhi[t][0]);
-            dlo[t][1] = split_lo_bf16x8(v + 8, dhi[t][1]);
-          }
-        }
-      }
-    });
-    // Deferred products of the last tile (no DMA is in flight any more).
-    if (pend) {
-      const int bl = (SPARSE ? tcnt - 1 : ntq - 1 - it0) % 3;
-      deferred(bl == 0 ? q_at(int_c<0>{}) : bl == 1 ? q_at(int_c<1>{}) : q_at(int_c<2>{}));
-    }
-  }
-
-  if (key < nk) {
-    uint16_t* row = (s_role ? dV : dK) + khead + (size_t)key * D;
-    const float f = s_role ? 1.0f : scale;
+    f32x16 acc[D / 32];  // dV^T (S wave) or dK^T (dP wave)
 #pragma unroll
     for (int e = 0; e < D / 32; ++e)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 o2;
-        o2[0] = pack_bf16x2(acc[e][4 * g + 0] * f, acc[e][4 * g + 1] * f);
-        o2[1] = pack_bf16x2(acc[e][4 * g + 2] * f, acc[e][4 * g + 3] * f);
-        *reinterpret_cast<u32x2*>(row + 32 * e + 8 * g + 4 * hh) = o2;
+      for (int r = 0; r < 16; ++r) acc[e][r] = 0.f;
+
+    const int ntq = (n + BQ - 1) / BQ;
+    const int it0 = CAUSAL ? max(0, k0 - coff) / BQ : 0;
+    // A tile whose queries all precede this key group is skipped (causal);
+    // both waves of a pair decide alike.
+    auto active = [&](int i) ATTN_INLINE { return !CAUSAL || (i * BQ + BQ - 1 >= kw0 - coff); };
+
+    // Block-sparse: the query tiles whose mask block (a 64-row tile is half of
+    // a 128-row block) may attend this key block (a workgroup's 128 keys are
+    // one mask block column), listed in LDS in increasing order.
+    uint32_t* const tlist = reinterpret_cast<uint32_t*>(smem + SMALL + 6 * TB + PXB);
+    int* const tcount = reinterpret_cast<int*>(tlist + kMaxSparseTiles);
+    int tcnt = 0;
+    if constexpr (SPARSE) {
+      const uint8_t* mcol = bmask + (size_t)bh * mask_stride + kb;
+      const int nbq = (n + kSparseBlock - 1) / kSparseBlock;
+      tcnt = build_tile_list([&](int i) ATTN_INLINE { return mcol[(size_t)(i >> 1) * nbq] != 0; }, it0, ntq, tlist,
+                             tcount, w, lane);
+    }
+
+    // Query rows past n load as zero (Q, dO, LSE, D), so they contribute
+    // nothing: P = 1 is finite and multiplies dO = 0 and dS = 0.
+    // A tile's batch of fetches: LSE and D rows (wave 0, one load each), then
+    // the Q and dO tiles (2 * IPW loads per wave).  Every tile issues the same
+    // batch (past the last tile: copies of the last one, never read), so the
+    // counts below hold on every path.
+    constexpr int SMALLN = 2;  // LSE and D loads of wave 0
+    auto dma = [&](int i, auto b) ATTN_INLINE {
+      if (w == 0) {
+        const uint32_t off = __builtin_amdgcn_readfirstlane((uint32_t)i * (BQ * 4));
+        const uint32_t sbase = (uint32_t)(uintptr_t)(ATTN_LDS char*)smem;
+        dma_row64_asm(rl, sbase + 512u * decltype(b)::value, off, lane);
+        dma_row64_asm(rd, sbase + 512u * decltype(b)::value + 256u, off, lane);
       }
+      dma_tile_asm<D, NW>(rq, q_at(b), i * BQ, w, lane);
+      dma_tile_asm<D, NW>(rdo, g_at(b), i * BQ, w, lane);
+    };
+    // Wave 0 scales the landed LSE row of buffer b to base 2 and negates the
+    // D row, in place; the tiles fetched after them (LATER loads) may still be
+    // in flight.
+    auto fix_small = [&](auto b, auto later) ATTN_INLINE {
+      if (w == 0) {
+        wait_vmem_upto<decltype(later)::value>();
+        asm volatile("" ::: "memory");
+        lse_at(b)[lane] *= kLog2e;
+        dsm_at(b)[lane] = -dsm_at(b)[lane];
+      }
+    };
+    // End of a tile: the batch of the next tile must have landed; the batch
+    // of the tile after it (issued last) stays in flight.
+    auto handover = [&]() ATTN_INLINE {
+      if (w == 0)
+        wait_vmem_upto<SMALLN + 2 * IPW>();
+      else
+        wait_vmem_upto<2 * IPW>();
+      barrier_lds();
+    };
+
+    float* px = pxs + grp * (2 * 4 * 64 * 4);
+
+    // Dropout keep bits of this lane's key for queries qbase + 0..3 (bit k).
+    // One generator call covers four consecutive keys of one query, so the
+    // four lanes of a quad (keys 4a .. 4a + 3) call it for the four queries
+    // and exchange words by a 4 x 4 transpose within the quad (DPP rotations).
+    auto quad_keep = [&](int qbase) ATTN_INLINE -> uint32_t {
+      const int tq = lane & 3;
+      const u32x4 wd = philox4x32_10((uint32_t)(kw0 + (l32 & ~3)) >> 2, (uint32_t)(qbase + tq), (uint32_t)bh,
+                                     dr.offset, dr.seed_lo, dr.seed_hi);
+      // y[k] = word tq of quad lane k: query qbase + k, this lane's key.
+      uint32_t y[4];
+      auto pick = [&](int idx) ATTN_INLINE {
+        return idx == 0 ? wd[0] : idx == 1 ? wd[1] : idx == 2 ? wd[2] : wd[3];
+      };
+#pragma unroll
+      for (int k = 0; k < 4; ++k) y[k] = 0u;
+      y[0] = tq == 0 ? wd[0] : y[0];
+      y[1] = tq == 1 ? wd[1] : y[1];
+      y[2] = tq == 2 ? wd[2] : y[2];
+      y[3] = tq == 3 ? wd[3] : y[3];
+      auto rot = [&](auto rc) ATTN_INLINE {
+        constexpr int RT = decltype(rc)::value;
+        // Lane s sends its word (s - RT) mod 4; lane r receives from lane
+        // (r + RT) mod 4 its word r.
+        const uint32_t x = pick((tq - RT) & 3);
+        constexpr int ctrl = ((0 + RT) & 3) | (((1 + RT) & 3) << 2) | (((2 + RT) & 3) << 4) | (((3 + RT) & 3) << 6);
+        const uint32_t r = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, 0xF, 0xF, false);
+        const int src = (tq + RT) & 3;
+        y[0] = src == 0 ? r : y[0];
+        y[1] = src == 1 ? r : y[1];
+        y[2] = src == 2 ? r : y[2];
+        y[3] = src == 3 ? r : y[3];
+      };
+      rot(int_c<1>{});
+      rot(int_c<2>{});
+      rot(int_c<3>{});
+      uint32_t bits = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) bits |= (y[k] >= dr.thr ? 1u : 0u) << k;
+      return bits;
+    };
+
+    // Products of P or dS for one half tile into dV or dK.  Where the half
+    // tile holds a weight (P, or scale * dS) >= 1/16 the values enter as hi +
+    // lo bf16 pairs (a
+    // single bf16 rounding, relative 2^-9, of a probability near 1 can move a
+    // column sum of magnitude > 4 by more than the output's own rounding
+    // leaves); each term is one call, with packed operands h[u].
+    auto acc_plain = [&](auto& tr, const uint16_t* bs, const bf16x8* h, int t) ATTN_INLINE {
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 a[2][D / 32];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) a[u][e] = tr.cols(bs, 32 * t + 16 * u, e);
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[0][e], h[0], acc[e]);
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[1][e], h[1], acc[e]);
+      pipeline_reads2<D / 16>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // The products of both half tiles (operands h0 for queries 0-31, h1 for
+    // 32-63) as one stream of 4 D / 16 MFMAs, so that operand reads run ahead
+    // across the two halves instead of stalling at the start of each.
+    auto acc_pair = [&](auto& tr, const uint16_t* bs, const bf16x8* h0, const bf16x8* h1) ATTN_INLINE {
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 a[4][D / 32];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) a[q][e] = tr.cols(bs, 16 * q, e);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bf16x8& hq = q < 2 ? h0[q & 1] : h1[q & 1];
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e) acc[e] = mfma32(a[q][e], hq, acc[e]);
+      }
+      pipeline_reads2<D / 8, 4>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // Wave-uniform test for the split.  P enters dV as it is; dS enters dK
+    // unscaled (the scale is applied to the accumulator at the end), so its
+    // threshold is divided by |scale|: a term's rounding error in the output
+    // is then bounded alike in both products.
+    const float tau = s_role ? kSplitThreshold : kSplitThreshold / fabsf(scale);
+    auto needs_split = [&](const float* vt) ATTN_INLINE {
+      float vmax = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) vmax = fmaxf(vmax, fabsf(vt[r]));
+      return __builtin_amdgcn_ballot_w64(vmax >= tau) != 0;
+    };
+    // Two independent MFMA chains (queries 0-31 and 32-63 of the tile) over
+    // the row-major tile `src`, with this wave's key-side fragments.
+    auto chains = [&](auto& tr, const uint16_t* src, f32x16& c0, f32x16& c1) ATTN_INLINE {
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 a0[D / 16], a1[D / 16];
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        a0[s] = tr.rows(src, 0, s);
+        a1[s] = tr.rows(src, 32, s);
+      }
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        c0 = mfma32(a0[s], bf[s], c0);
+        c1 = mfma32(a1[s], bf[s], c1);
+      }
+      pipeline_reads<D / 8>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // Tile loop skeleton shared by both roles (same barriers in both): tile i
+    // lives in buffer b = (i - it0) mod 3.  body(b, i, mid) does the role's
+    // work on tile i and calls mid() exactly once, between its two halves.
+    auto run_dense = [&](auto&& body) ATTN_INLINE {
+      auto step = [&](auto b, int i) ATTN_INLINE {
+        constexpr int B = decltype(b)::value;
+        body(b, i, [&]() ATTN_INLINE {
+          fix_small(int_c<(B + 1) % 3>{}, int_c<2 * IPW>{});  // LSE of tile i + 1
+          barrier_lds();  // P of tile i is published; reads of tile i - 1 are done
+          dma(min(i + 2, ntq - 1), int_c<(B + 2) % 3>{});
+        });
+        handover();
+      };
+      dma(it0, int_c<0>{});
+      dma(min(it0 + 1, ntq - 1), int_c<1>{});
+      fix_small(int_c<0>{}, int_c<SMALLN + 4 * IPW>{});
+      handover();
+      for (int it = it0; it < ntq; it += 3) {
+        step(int_c<0>{}, it);
+        if (it + 1 >= ntq) break;
+        step(int_c<1>{}, it + 1);
+        if (it + 2 >= ntq) break;
+        step(int_c<2>{}, it + 2);
+      }
+    };
+    // The same sequence over the listed tiles: position p holds tile T(p) in
+    // buffer p mod 3.
+    auto run_list = [&](auto&& body) ATTN_INLINE {
+      auto T = [&](int p) ATTN_INLINE { return __builtin_amdgcn_readfirstlane((int)tlist[p]); };
+      auto step = [&](auto b, int p) ATTN_INLINE {
+        constexpr int B = decltype(b)::value;
+        body(b, T(p), [&]() ATTN_INLINE {
+          fix_small(int_c<(B + 1) % 3>{}, int_c<2 * IPW>{});  // LSE of the next tile
+          barrier_lds();  // P of this tile is published; reads of the previous one are done
+          dma(T(min(p + 2, tcnt - 1)), int_c<(B + 2) % 3>{});
+        });
+        handover();
+      };
+      if (tcnt == 0) return;
+      dma(T(0), int_c<0>{});
+      dma(T(min(1, tcnt - 1)), int_c<1>{});
+      fix_small(int_c<0>{}, int_c<SMALLN + 4 * IPW>{});
+      handover();
+      for (int p = 0; p < tcnt; p += 3) {
+        step(int_c<0>{}, p);
+        if (p + 1 >= tcnt) break;
+        step(int_c<1>{}, p + 1);
+        if (p + 2 >= tcnt) break;
+        step(int_c<2>{}, p + 2);
+      }
+    };
+    auto run = [&](auto&& body) ATTN_INLINE {
+      if constexpr (SPARSE)
+        run_list(body);
+      else
+        run_dense(body);
+      wait_vmem();  // no fetch outlives the loop
+    };
+
+    if (s_role) {
+      // S wave: S = Q K^T, P = exp(S - LSE) published through LDS, then
+      // dV^T += dO^T P.
+      const TileReader<D, 0, GSHIFT> TR(lane);
+      run([&](auto b, int i, auto&& mid) ATTN_INLINE {
+        const bool act = active(i);
+        float v[2][16];
+        if (act) {
+          const float* lse2s = lse_at(b);
+          f32x16 c0, c1;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            c0[r] = 0.f;
+            c1[r] = 0.f;
+          }
+          chains(TR, q_at(b), c0, c1);
+          // Exponent arguments; on the diagonal tiles only (a wave-uniform
+          // branch), entries whose key follows the query become -inf, whose
+          // exp2 is 0.  Written as selects inside the exponential loop, the
+          // mask ran on every tile.
+          float x[2][16];
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse2s[32 * t + 8 * g + 4 * hh]);
+#pragma unroll
+              for (int k = 0; k < 4; ++k) x[t][4 * g + k] = fmaf(t == 0 ? c0[4 * g + k] : c1[4 * g + k], sl2e, -l4[k]);
+            }
+          if (CAUSAL && i * BQ < kw0 + 31 - coff) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int q = i * BQ + 32 * t + crow(r, hh);
+                x[t][r] = key > q + coff ? -INFINITY : x[t][r];
+              }
+          }
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int qbase = i * BQ + 32 * t + 8 * g + 4 * hh;  // queries qbase + k of registers 4g + k
+              uint32_t keep = 0xFu;
+              if constexpr (DROP) keep = quad_keep(qbase);
+              f32x4 o;
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const float pv = fast_exp2(x[t][4 * g + k]);
+                if constexpr (DROP) {
+                  // dV takes the dropped, rescaled probability; the dP wave
+                  // gets P with the keep bit in the sign (P >= 0).
+                  const bool kept = (keep >> k) & 1u;
+                  v[t][4 * g + k] = kept ? pv * dr.keep_scale : 0.f;
+                  o[k] = kept ? pv : -pv;
+                } else {
+                  v[t][4 * g + k] = pv;
+                  o[k] = pv;
+                }
+              }
+              *reinterpret_cast<f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]) = o;
+            }
+        }
+        mid();
+        if (act) {
+          // hi terms always (both halves as one stream), lo terms only where
+          // the half tile needs them: the accumulators are only ever updated in
+          // place (no alternative paths that the register allocator would join
+          // with copies).
+          const bf16x8 h0[2] = {pack_bf16x8(v[0]), pack_bf16x8(v[0] + 8)};
+          const bf16x8 h1[2] = {pack_bf16x8(v[1]), pack_bf16x8(v[1] + 8)};
+          const bool sp0 = needs_split(v[0]), sp1 = needs_split(v[1]);
+          acc_pair(TR, g_at(b), h0, h1);
+          if (sp0) {
+            const bf16x8 l[2] = {split_lo_bf16x8(v[0], h0[0]), split_lo_bf16x8(v[0] + 8, h0[1])};
+            acc_plain(TR, g_at(b), l, 0);
+          }
+          if (sp1) {
+            const bf16x8 l[2] = {split_lo_bf16x8(v[1], h1[0]), split_lo_bf16x8(v[1] + 8, h1[1])};
+            acc_plain(TR, g_at(b), l, 1);
+          }
+        }
+      });
+    } else {
+      // dP wave: dP = dO V^T accumulated onto -D (registers run over queries),
+      // so it ends with dP - D; after P arrives, dS = P * (dP - D).  The dK^T
+      // += Q^T dS products of each half tile are deferred to the next tile's
+      // first half, with dS kept packed in registers (hi and, where the half
+      // tile needs the split, lo bf16 terms).
+      const TileReader<D, GSHIFT, 0> TR(lane);
+      bf16x8 dhi[2][2], dlo[2][2];
+      bool pend = false, spl0 = false, spl1 = false;
+      auto deferred = [&](const uint16_t* qs) ATTN_INLINE {
+        acc_pair(TR, qs, dhi[0], dhi[1]);
+        if (spl0) acc_plain(TR, qs, dlo[0], 0);
+        if (spl1) acc_plain(TR, qs, dlo[1], 1);
+      };
+      run([&](auto b, int i, auto&& mid) ATTN_INLINE {
+        constexpr int BP = (decltype(b)::value + 2) % 3;  // buffer of the previous tile
+        const bool act = active(i);
+        // The accumulators start from -D (with dropout from 0: dP is needed
+        // alone, dS = P (Z dP / (1 - p) - D)).  The -D rows are read before
+        // the deferred products, which hide the LDS latency; read just before
+        // the chains, the first product waited for them.
+        f32x16 c0, c1;
+        {
+          const float* dsms = dsm_at(b);
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 d0 = *reinterpret_cast<const f32x4*>(&dsms[8 * g + 4 * hh]);
+            const f32x4 d1 = *reinterpret_cast<const f32x4*>(&dsms[32 + 8 * g + 4 * hh]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              c0[4 * g + k] = DROP ? 0.f : d0[k];
+              c1[4 * g + k] = DROP ? 0.f : d1[k];
+            }
+          }
+        }
+        if (pend) deferred(q_at(int_c<BP>{}));
+        if (act) chains(TR, g_at(b), c0, c1);
+        mid();
+        pend = act;
+        if (act) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            float v[16];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 p4 = *reinterpret_cast<const f32x4*>(&px[((t * 4 + g) * 64 + lane) * 4]);
+              if constexpr (DROP) {
+                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dsm_at(b)[32 * t + 8 * g + 4 * hh]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  const float dpv = t == 0 ? c0[4 * g + k] : c1[4 * g + k];
+                  const bool kept = (__float_as_uint(p4[k]) >> 31) == 0u;
+                  v[4 * g + k] = fabsf(p4[k]) * ((kept ? dpv * dr.keep_scale : 0.f) + d4[k]);  // d4 = -D
+                }
+              } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[4 * g + k] = (t == 0 ? c0[4 * g + k] : c1[4 * g + k]) * p4[k];
+              }
+            }
+            const bool sp = needs_split(v);
+            (t == 0 ? spl0 : spl1) = sp;
+            dhi[t][0] = pack_bf16x8(v);
+            dhi[t][1] = pack_bf16x8(v + 8);
+            if (sp) {
+              dlo[t][0] = split_lo_bf16x8(v, dhi[t][0]);
+              dlo[t][1] = split_lo_bf16x8(v + 8, dhi[t][1]);
+            }
+          }
+        }
+      });
+      // Deferred products of the last tile (no DMA is in flight any more).
+      if (pend) {
+        const int bl = (SPARSE ? tcnt - 1 : ntq - 1 - it0) % 3;
+        deferred(bl == 0 ? q_at(int_c<0>{}) : bl == 1 ? q_at(int_c<1>{}) : q_at(int_c<2>{}));
+      }
+    }
+
+    if (key < nk) {
+      uint16_t* row = (s_role ? dV : dK) + khead + (size_t)key * D;
+      const float f = s_role ? 1.0f : scale;
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2 o2;
+          o2[0] = pack_bf16x2(acc[e][4 * g + 0] * f, acc[e][4 * g + 1] * f);
+          o2[1] = pack_bf16x2(acc[e][4 * g + 2] * f, acc[e][4 * g + 3] * f);
+          *reinterpret_cast<u32x2*>(row + 32 * e + 8 * g + 4 * hh) = o2;
+        }
+    }
   }
 }
 
@@ -937,7 +954,10 @@ hipError_t launch_dkdv(const BwdArgs& a) {
   const int n = (int)a.n;
   const int nk = QK ? (int)a.nk : n;
   const int nkb = (nk + 127) / 128;
-  const int total = (int)(a.bh * nkb);
+  // Causal, square, dense, no dropout: one workgroup per pair of mirrored
+  // key blocks (see bwd_kv_kernel).
+  constexpr bool PAIRED = CAUSAL && !SPARSE && !QK && !DROP;
+  const int total = (int)(a.bh * (PAIRED ? (nkb + 1) / 2 : nkb));
   hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, SPARSE, QK, DROP>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e,
