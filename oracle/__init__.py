@@ -22,8 +22,9 @@ Modules:
 
 * :mod:`oracle.attention` -- the definition (S, P, O, LSE) and its
   textbook chain-rule gradients, materialising S and P.
-* :mod:`oracle.online` -- the pages' tiled online-softmax forward, kept only
-  to pin the definition (tiled == one-shot) and to replay the pages' worked
+* :mod:`oracle.online` -- softmax attention from per-part states (m, l and
+  the unnormalised output) and the two-block merge rule, kept only to pin the
+  definition (block-wise == one-shot) and to replay the pages' worked
   examples step by step.
 * :mod:`oracle.blocksparse` -- the same definition under a block mask (the
   block-sparse variant named in "Experiments & Results" on the Paper Notes

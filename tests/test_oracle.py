@@ -123,6 +123,24 @@ def test_tiled_online_softmax_equals_one_shot(causal, n):
         np.testing.assert_allclose(lse, l_ref, rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_merge_rule_over_uneven_partitions_and_any_grouping(causal):
+    """The two-block merge rule ("Tiling: Block-by-Block Softmax") folded over
+    random uneven cuts of the keys, left to right or as a balanced tree, gives
+    the one-shot softmax (the merge is associative)."""
+    n, d = 97, 6
+    q, k, v = _rand(61, n, d), _rand(62, n, d), _rand(63, n, d)
+    o_ref, l_ref = A.forward_head(q, k, v, causal, 0.7)
+    rng = np.random.default_rng(64)
+    for trial in range(6):
+        cuts = np.sort(rng.choice(np.arange(1, n), size=int(rng.integers(1, 12)), replace=False))
+        for tree in (False, True):
+            o, lse = OL.flash_forward_head(q, k, v, causal, 0.7, block_q=int(rng.integers(1, 40)), key_bounds=cuts,
+                                           tree=tree)
+            np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse, l_ref, rtol=0, atol=1e-12)
+
+
 def test_single_key_and_first_causal_row():
     q, k, v = _rand(7, 1, 4), _rand(8, 1, 4), _rand(9, 1, 4)
     o, lse = A.forward_head(q, k, v, False, 0.3)
