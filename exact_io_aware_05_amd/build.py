@@ -88,5 +88,49 @@ def build(verbose=False):
     return LIB
 
 
+# Host-side sanitizer flags for hipcc: each -fsanitize= behind -Xarch_host, so
+# only the host code (argument validation, dispatch) is instrumented and the
+# device code is compiled as usual.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(dest):
+    """AddressSanitizer + UndefinedBehaviorSanitizer builds of the host code, for
+    checks on a CPU: ``dest/libattn_san.so`` (every csrc/*.hip file, host side
+    instrumented by clang's sanitizers; run under clang's ASan runtime) and
+    ``dest/libattn_cpu_san.so`` (attn_cpu.cpp under gcc's sanitizers; run under
+    gcc's libasan).  Returns the two paths."""
+    os.makedirs(dest, exist_ok=True)
+    objdir = os.path.join(dest, "obj")
+    os.makedirs(objdir, exist_ok=True)
+    flags = [f"--offload-arch={ARCH}", "-O1", "-g", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include")]
+    flags += DEVICE_FLAGS + SAN_HOST
+
+    def comp(src):
+        obj = os.path.join(objdir, os.path.basename(src)[:-4] + ".o")
+        r = subprocess.run([HIPCC, "-c", src, "-o", obj] + flags, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized) failed for {src}:\n{r.stderr}")
+        return obj
+
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(comp, srcs))
+    hip_lib = os.path.join(dest, "libattn_san.so")
+    r = subprocess.run([HIPCC, "-shared", "-o", hip_lib] + objs + [f"--offload-arch={ARCH}"] + SAN_HOST
+                       + ["-Xarch_host", "-shared-libsan"], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized) failed:\n{r.stderr}")
+    cpu_lib = os.path.join(dest, "libattn_cpu_san.so")
+    cmd = [CXX, "-O1", "-g", "-mavx2", "-mfma", "-fopenmp", "-fPIC", "-shared", "-std=c++17",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           "-I", os.path.join(ROOT, "include"), os.path.join(CSRC, "attn_cpu.cpp"), "-o", cpu_lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ (sanitized) failed:\n{r.stderr}")
+    return hip_lib, cpu_lib
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
