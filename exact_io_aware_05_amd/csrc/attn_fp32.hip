@@ -26,73 +26,153 @@ __device__ __forceinline__ float quad_sum(float x) {
   return x;
 }
 
+// Forward: a workgroup owns 16 queries of one head; each of its four waves
+// holds all 16 (four lanes per query) and takes every fourth key of each
+// 64-key tile, so a wave's running (m, l, O) covers a quarter of the keys.
+// The four partial states are merged at the end with the two-block rule of
+// "Tiling: Block-by-Block Softmax" (Paper Notes): m = max m_w, l = sum_w
+// e^(m_w - m) l_w, O = sum_w e^(m_w - m) O_w / l.  Lane c of a query holds the
+// features 4 (c + 4 i) .. 4 (c + 4 i) + 3 (i = 0 .. D / 16 - 1), so a key row
+// is read from LDS with D / 16 16-byte reads whose four distinct addresses per
+// wave fall in distinct banks.  The next tile's K and V rows are loaded into
+// registers while the current tile is used.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int n, int nqb, float sl2e) {
-  constexpr int BQ = 64, BK = 64, DQ = D / 4;
+  constexpr int BQ = 16, BK = 64, NC = D / 16;  // NC: 4-float chunks per lane
+  constexpr int PRE = BK * D / 4 / 256;         // 4-float chunks of a tile per thread (K, and V alike)
   __shared__ __attribute__((aligned(16))) float ks[BK * D];
   __shared__ __attribute__((aligned(16))) float vs[BK * D];
-  const int tid = threadIdx.x, c = tid & 3, ql = tid >> 2;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 3, ql = lane >> 2;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x / nqb, qb = blockIdx.x % nqb;
   const int qrow = qb * BQ + ql;
   const size_t head = (size_t)bh * n * D;
   const float* Kh = K + head;
   const float* Vh = V + head;
 
-  float qv[DQ], acc[DQ];
+  f32x4 qv[NC], acc[NC];
 #pragma unroll
-  for (int i = 0; i < DQ; ++i) {
-    qv[i] = qrow < n ? Q[head + (size_t)qrow * D + 4 * i + c] : 0.f;
-    acc[i] = 0.f;
+  for (int i = 0; i < NC; ++i) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    qv[i] = qrow < n ? *reinterpret_cast<const f32x4*>(Q + head + (size_t)qrow * D + 4 * (c + 4 * i)) : z;
+    acc[i] = z;
   }
   float m = -INFINITY, l = 0.f;
   const int kend = CAUSAL ? min(n, qb * BQ + BQ) : n;
-  for (int j0 = 0; j0 < kend; j0 += BK) {
-    __syncthreads();
-    for (int idx = tid; idx < BK * D / 4; idx += 256) {
-      const int row = idx / (D / 4), c4 = idx % (D / 4), key = j0 + row;
+  const int ntiles = (kend + BK - 1) / BK;
+
+  // Thread tid stages chunks tid + 256 r of a tile (row = chunk / (D / 4)).
+  f32x4 kn[PRE], vn[PRE];
+  auto load = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < PRE; ++r) {
+      const int idx = tid + 256 * r, row = idx / (D / 4), c4 = idx % (D / 4), key = j0 + row;
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(&ks[row * D + 4 * c4]) =
-          key < n ? *reinterpret_cast<const f32x4*>(Kh + (size_t)key * D + 4 * c4) : z;
-      *reinterpret_cast<f32x4*>(&vs[row * D + 4 * c4]) =
-          key < n ? *reinterpret_cast<const f32x4*>(Vh + (size_t)key * D + 4 * c4) : z;
+      kn[r] = key < n ? *reinterpret_cast<const f32x4*>(Kh + (size_t)key * D + 4 * c4) : z;
+      vn[r] = key < n ? *reinterpret_cast<const f32x4*>(Vh + (size_t)key * D + 4 * c4) : z;
+    }
+  };
+  if (ntiles > 0) load(0);
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * BK;
+    __syncthreads();  // every wave is done with the previous tile
+#pragma unroll
+    for (int r = 0; r < PRE; ++r) {
+      *reinterpret_cast<f32x4*>(&ks[4 * (tid + 256 * r)]) = kn[r];
+      *reinterpret_cast<f32x4*>(&vs[4 * (tid + 256 * r)]) = vn[r];
     }
     __syncthreads();
-    float s[BK];
+    if (t + 1 < ntiles) load(j0 + BK);
+    // This wave's keys of the tile: rows w, w + 4, ..., w + 60.
+    float s[BK / 4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int jj = 0; jj < BK; ++jj) {
+    for (int jj = 0; jj < BK / 4; ++jj) {
+      const int row = 4 * jj + w;
       float part = 0.f;
 #pragma unroll
-      for (int i = 0; i < DQ; ++i) part = fmaf(qv[i], ks[jj * D + 4 * i + c], part);
+      for (int i = 0; i < NC; ++i) {
+        const f32x4 kk = *reinterpret_cast<const f32x4*>(&ks[row * D + 4 * (c + 4 * i)]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) part = fmaf(qv[i][e], kk[e], part);
+      }
       const float x = quad_sum(part) * sl2e;
-      const int key = j0 + jj;
+      const int key = j0 + row;
       const bool dead = key >= n || (CAUSAL && key > qrow);
       s[jj] = dead ? -INFINITY : x;
       mx = fmaxf(mx, s[jj]);
     }
-    // Tile 0 always holds key 0, visible to every query: m_new is finite.
     const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
-    l *= alpha;
+    // A wave may have seen no visible key of this query yet (causal): its
+    // state stays (-inf, 0, 0).
+    if (m_new != -INFINITY) {
+      const float alpha = fast_exp2(m - m_new);  // 0 while m = -inf
+      l *= alpha;
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) acc[i] *= alpha;
+      for (int i = 0; i < NC; ++i) acc[i] *= alpha;
 #pragma unroll
-    for (int jj = 0; jj < BK; ++jj) {
-      const float p = fast_exp2(s[jj] - m_new);
-      l += p;
+      for (int jj = 0; jj < BK / 4; ++jj) {
+        const int row = 4 * jj + w;
+        const float p = fast_exp2(s[jj] - m_new);
+        l += p;
 #pragma unroll
-      for (int i = 0; i < DQ; ++i) acc[i] = fmaf(p, vs[jj * D + 4 * i + c], acc[i]);
+        for (int i = 0; i < NC; ++i) {
+          const f32x4 vv = *reinterpret_cast<const f32x4*>(&vs[row * D + 4 * (c + 4 * i)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(p, vv[e], acc[i][e]);
+        }
+      }
+      m = m_new;
     }
-    m = m_new;
   }
-  if (qrow < n) {
-    const float inv = 1.0f / l;
+
+  // Merge the four waves' states through LDS: wave w's unnormalised output
+  // rows in the K tile area, (m, l) per query in the V tile area.
+  __syncthreads();
+  float* const ro = ks;  // [w][ql][D]
+  float* const rm = vs;  // [w][ql][2]
+  static_assert(4 * BQ * D <= BK * D && 4 * BQ * 2 <= BK * D, "merge areas fit the tiles");
 #pragma unroll
-    for (int i = 0; i < DQ; ++i) O[head + (size_t)qrow * D + 4 * i + c] = acc[i] * inv;
-    if (c == 0) LSE[(size_t)bh * n + qrow] = (m + fast_log2(l)) * kLn2;
+  for (int i = 0; i < NC; ++i) *reinterpret_cast<f32x4*>(&ro[(w * BQ + ql) * D + 4 * (c + 4 * i)]) = acc[i];
+  if (c == 0) {
+    rm[(w * BQ + ql) * 2] = m;
+    rm[(w * BQ + ql) * 2 + 1] = l;
   }
+  __syncthreads();
+  if (w != 0 || qrow >= n) return;
+  float mw[4], lw[4];
+  float mt = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    mw[u] = rm[(u * BQ + ql) * 2];
+    lw[u] = rm[(u * BQ + ql) * 2 + 1];
+    mt = fmaxf(mt, mw[u]);
+  }
+  // Key 0 (or, past the diagonal, the query's own key) is visible to every
+  // query, so mt is finite.
+  float wt[4], lt = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    wt[u] = mw[u] == -INFINITY ? 0.f : fast_exp2(mw[u] - mt);
+    lt += wt[u] * lw[u];
+  }
+  const float inv = 1.0f / lt;
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&ro[(u * BQ + ql) * D + 4 * (c + 4 * i)]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = fmaf(wt[u], a[e], o[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] *= inv;
+    *reinterpret_cast<f32x4*>(O + head + (size_t)qrow * D + 4 * (c + 4 * i)) = o;
+  }
+  if (c == 0) LSE[(size_t)bh * n + qrow] = (mt + fast_log2(lt)) * kLn2;
 }
 
 // dK, dV for a block of 64 keys; streams query tiles of 32 rows.
@@ -234,7 +314,7 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
 
 template <int D, bool CAUSAL>
 hipError_t fwd_f32_t(const FwdArgs& a) {
-  const int nqb = (int)((a.n + 63) / 64);
+  const int nqb = (int)((a.n + 15) / 16);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqb)), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.n, nqb,
                      a.scale * kLog2e);
