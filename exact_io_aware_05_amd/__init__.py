@@ -17,6 +17,8 @@ Entry points carry the C names:
   lengths (bottom-right causal alignment), with split-K/V for the forward
 * :func:`attn_fwd_dropout`, :func:`attn_bwd_dropout` -- the same with dropout
   on the probabilities (mask from a counter-based generator, not stored)
+* :func:`attn_fwd_kpad`, :func:`attn_bwd_kpad` -- the same with a key padding
+  mask (per-sequence key lengths)
 * :func:`attn_bwd_workspace_bytes`, :func:`attn_status_string`
 * :func:`lib` -- the raw ``ctypes.CDLL``.
 
@@ -42,6 +44,8 @@ __all__ = [
     "attn_bwd_qk",
     "attn_fwd_dropout",
     "attn_bwd_dropout",
+    "attn_fwd_kpad",
+    "attn_bwd_kpad",
     "attn_bwd_workspace_bytes",
     "attn_status_string",
     "lib",
@@ -118,6 +122,11 @@ def lib():
     L.attn_bwd_dq_dsum.restype = i32
     L.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp]
     L.attn_bwd_noalloc.restype = i32
+    L.attn_fwd_kpad.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp, vp]
+    L.attn_fwd_kpad.restype = i32
+    L.attn_bwd_kpad.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp, vp,
+                                ctypes.c_size_t, vp]
+    L.attn_bwd_kpad.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -517,4 +526,66 @@ def attn_bwd_dropout(q, k, v, o, do, lse, p_drop, seed, offset=0, causal=False, 
     )
     if st != 0:
         raise AttnError(st, "attn_bwd_dropout")
+    return dq, dk, dv
+
+
+def _key_len(key_len, B, device):
+    torch = _torch()
+    if not (torch.is_tensor(key_len) and key_len.dtype == torch.int32 and key_len.shape == (B,)
+            and key_len.device == device and key_len.is_contiguous()):
+        raise ValueError(f"key_len must be a contiguous int32 tensor of shape ({B},) on {device}")
+    return key_len
+
+
+def attn_fwd_kpad(q, k, v, key_len, causal=False, scale=None, out=None, lse=None):
+    """Forward with a key padding mask: batch b attends only its keys
+    j < key_len[b] (int32 [B] on the same GPU; clamped to [0, N] by the
+    kernels).  Returns (o, lse); a row that sees no key gets o = 0 and
+    lse = -inf."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v)], q.shape, q.dtype, q.device)
+    key_len = _key_len(key_len, B, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check([("out", out)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    st = lib().attn_fwd_kpad(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, _dtype_code(q),
+        int(bool(causal)), float(scale), key_len.data_ptr(), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_fwd_kpad")
+    return out, lse
+
+
+def attn_bwd_kpad(q, k, v, o, do, lse, key_len, causal=False, scale=None, workspace=None, grads=None):
+    """Backward of :func:`attn_fwd_kpad` (same key_len, causal, scale);
+    returns (dq, dk, dv), with dk = dv = 0 for the padded keys."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v), ("o", o), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    key_len = _key_len(key_len, B, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    _check([("dq", dq), ("dk", dk), ("dv", dv)], q.shape, q.dtype, q.device)
+    st = lib().attn_bwd_kpad(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), B, H, N, d, code, int(bool(causal)), float(scale), key_len.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_bwd_kpad")
     return dq, dk, dv

@@ -315,6 +315,49 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
   return run_bwd(a, dtype == ATTN_BF16);
 }
 
+int attn_fwd_kpad(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                  int64_t N, int64_t d, int dtype, int causal, float scale, const int32_t* key_len, void* stream) {
+  if (!q || !k || !v || !o || !lse || !key_len) return ATTN_E_NULL;
+  if (!all16(q, k, v, o) || !al4(lse) || !al4(key_len)) return ATTN_E_ALIGN;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = B * H;
+  a.n = N;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  a.klen = key_len;
+  a.heads = (int)H;
+  const hipError_t e = dtype == ATTN_BF16 ? attn::fwd_bf16(a) : attn::fwd_f32(a);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_bwd_kpad(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                  void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, int causal,
+                  float scale, const int32_t* key_len, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !key_len) return ATTN_E_NULL;
+  if (!all16(q, k, v, o, dout, dq, dk, dv) || !al4(lse) || !al4(key_len)) return ATTN_E_ALIGN;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, dtype) ||
+      ((uintptr_t)workspace & 255) != 0)
+    return ATTN_E_WORKSPACE;
+  attn::BwdArgs a =
+      make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
+  a.klen = key_len;
+  a.heads = (int)H;
+  return run_bwd(a, dtype == ATTN_BF16);
+}
+
 int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                          int64_t N, int64_t d, int dtype, int causal, float scale, const uint8_t* block_mask,
                          int64_t mask_head_stride, void* stream) {

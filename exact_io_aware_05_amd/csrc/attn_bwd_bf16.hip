@@ -110,7 +110,8 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
                                                         uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                                                         int n, int nkb, int total, float scale, float sl2e,
                                                         const uint8_t* __restrict__ bmask, long long mask_stride,
-                                                        int nk_arg, int coff_arg, DropArgs dr) {
+                                                        int nk_arg, int coff_arg, DropArgs dr,
+                                                        const int* __restrict__ klen, int heads) {
   constexpr int NW = 8, BKV = 128, BQ = 64;
   constexpr int TB = BQ * D * 2;  // bytes per 64-row tile
   constexpr int IPW = (D / 8) / NW;  // DMA loads per wave per tile
@@ -173,6 +174,21 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 
     const size_t head = (size_t)bh * (size_t)n * D;
     const size_t khead = (size_t)bh * (size_t)nk * D;
+    // Key padding (square lengths): keys from nkv on are masked for every
+    // query, so their dK and dV are zero; a block of padded keys only writes
+    // those zeros.
+    const int nkv = QK ? nk : padded_keys(klen, heads, bh, n);
+    if (k0 >= nkv) {
+      if (key < nk) {
+        uint16_t* row = (s_role ? dV : dK) + khead + (size_t)key * D;
+        const u32x2 z = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) *reinterpret_cast<u32x2*>(row + 32 * e + 8 * g + 4 * hh) = z;
+      }
+      continue;
+    }
     const uint32_t head_bytes = (uint32_t)n * D * 2u;
     // Q and dO tiles are fetched through inline asm (dma_tile_asm): the
     // compiler would otherwise make LDS accesses of one buffer wait for the
@@ -590,6 +606,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
     if (key < nk) {
       uint16_t* row = (s_role ? dV : dK) + khead + (size_t)key * D;
       const float f = s_role ? 1.0f : scale;
+      const bool live = key < nkv;  // a padded key of a partly padded block: zero
 #pragma unroll
       for (int e = 0; e < D / 32; ++e)
 #pragma unroll
@@ -597,6 +614,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
           u32x2 o2;
           o2[0] = pack_bf16x2(acc[e][4 * g + 0] * f, acc[e][4 * g + 1] * f);
           o2[1] = pack_bf16x2(acc[e][4 * g + 2] * f, acc[e][4 * g + 3] * f);
+          if (!live) o2[0] = o2[1] = 0u;
           *reinterpret_cast<u32x2*>(row + 32 * e + 8 * g + 4 * hh) = o2;
         }
     }
@@ -619,7 +637,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
                                                            int nb, int nk_arg, int coff_arg, DropArgs dr,
                                                            int kchunk, float* __restrict__ dqpart,
                                                            const uint16_t* __restrict__ Osrc,
-                                                           float* __restrict__ Dout) {
+                                                           float* __restrict__ Dout,
+                                                           const int* __restrict__ klen, int heads) {
   constexpr int BR = NW * 32, BC = 64;
 
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[BC * D];
@@ -661,8 +680,10 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   // of the split is the same problem on keys kb .. kb + nk - 1: K and V start
   // kb rows later and the causal offset drops by kb (rows that see no key of
   // the chunk get a zero partial).
+  // Key padding (square lengths): keys from padded_keys(..) on are masked
+  // like keys past the end.
   const int kb = split ? ks * kchunk : 0;
-  const int nk = QK ? (split ? min(kchunk, nk_arg - kb) : nk_arg) : n;
+  const int nk = QK ? (split ? min(kchunk, nk_arg - kb) : nk_arg) : padded_keys(klen, heads, bh, n);
   const int coff = (QK && CAUSAL) ? coff_arg - kb : 0;
   const size_t head = (size_t)bh * (size_t)n * D;
   const size_t khead = (size_t)bh * (size_t)(QK ? nk_arg : n) * D + (size_t)kb * D;
@@ -771,7 +792,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kj = j0 + 32 * t + crow(r, hh);
-            x[r] = (CAUSAL ? kj > qrow + coff : kj >= nk) ? -INFINITY : x[r];
+            x[r] = (kj >= nk || (CAUSAL && kj > qrow + coff)) ? -INFINITY : x[r];
           }
         }
 #pragma unroll
@@ -863,7 +884,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
     // the register allocator copy the dQ accumulators on every tile.  The
     // remaining tiles (the last one, or the diagonal ones) follow in a loop
     // with the checks.
-    const int nfree = CAUSAL ? min(ntiles, max(0, (q0 + coff + 1) / BC)) : ntiles - 1;
+    // (Under key padding a causal tile before the first row can still hold
+    // padded keys: free tiles also lie wholly below nk.)
+    const int nfree = CAUSAL ? min(min(ntiles, nk / BC), max(0, (q0 + coff + 1) / BC)) : ntiles - 1;
     auto fetch = [&](uint16_t* ks, uint16_t* vs, int jt) ATTN_INLINE {
       dma_tile<D, NW>(rk, ks, jt * BC, w, lane);
       dma_tile<D, NW>(rv, vs, jt * BC, w, lane);
@@ -961,7 +984,7 @@ hipError_t launch_dkdv(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, SPARSE, QK, DROP>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e,
-                     a.bmask, (long long)a.mask_stride, nk, nk - n, a.drop);
+                     a.bmask, (long long)a.mask_stride, nk, nk - n, a.drop, a.klen, a.heads);
   return hipGetLastError();
 }
 
@@ -987,7 +1010,7 @@ hipError_t launch_dq(const BwdArgs& a) {
                      a.scale,
                      a.scale * kLog2e, a.bmask, (long long)a.mask_stride, nb, nk, nk - n, a.drop,
                      split ? a.kchunk : 0, split ? a.dqpart : nullptr,
-                     form_d ? (const uint16_t*)a.o : nullptr, form_d ? a.dsum : nullptr);
+                     form_d ? (const uint16_t*)a.o : nullptr, form_d ? a.dsum : nullptr, a.klen, a.heads);
   if (!split) return hipGetLastError();
   const long long n4 = a.bh * a.n * (long long)D / 4;
   const long long blocks = std::min<long long>((n4 + 255) / 256, 4096);

@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
                                                           const float* __restrict__ LSE,
                                                           const float* __restrict__ Dsum, uint16_t* __restrict__ dK,
                                                           uint16_t* __restrict__ dV, int n, int nkb, int total,
-                                                          float scale, float sl2e, float tau_ds) {
+                                                          float scale, float sl2e, float tau_ds,
+                                                          const int* __restrict__ klen, int heads) {
   constexpr int D = 64, NW = 4, BKV = 32 * NW, BQ = 64;
   constexpr int TB = BQ * D * 2;     // bytes per 64-row tile
   constexpr int IPW = (D / 8) / NW;  // DMA loads per wave per tile
@@ -115,6 +116,22 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
   const int key = kw0 + l32;
 
   const size_t head = (size_t)bh * (size_t)n * D;
+  // Key padding: keys from nkv on are masked for every query, so their dK
+  // and dV are zero; a block of padded keys only writes those zeros.
+  const int nkv = padded_keys(klen, heads, bh, n);
+  if (k0 >= nkv) {
+    if (key < n) {
+      const u32x2 z = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < D / 32; ++e)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          *reinterpret_cast<u32x2*>(dV + head + (size_t)key * D + 32 * e + 8 * g + 4 * hh) = z;
+          *reinterpret_cast<u32x2*>(dK + head + (size_t)key * D + 32 * e + 8 * g + 4 * hh) = z;
+        }
+    }
+    return;
+  }
   const uint32_t head_bytes = (uint32_t)n * D * 2u;
   const RsrcWords rq = rsrc_words(Q + head, head_bytes);
   const RsrcWords rdo = rsrc_words(dO + head, head_bytes);
@@ -312,6 +329,7 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
   int le = threadIdx.x & 63;
   asm volatile("" : "+v"(le));
   const int keye = kw0 + (le & 31), hhe = le >> 5;
+  const bool live = keye < nkv;  // a padded key of a partly padded block: zero
   if (keye < n) {
     uint16_t* vrow = dV + head + (size_t)keye * D;
     uint16_t* krow = dK + head + (size_t)keye * D;
@@ -324,6 +342,7 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
         v2[1] = pack_bf16x2(dva[e][4 * g + 2], dva[e][4 * g + 3]);
         k2[0] = pack_bf16x2(dka[e][4 * g + 0] * scale, dka[e][4 * g + 1] * scale);
         k2[1] = pack_bf16x2(dka[e][4 * g + 2] * scale, dka[e][4 * g + 3] * scale);
+        if (!live) v2[0] = v2[1] = k2[0] = k2[1] = 0u;
         *reinterpret_cast<u32x2*>(vrow + 32 * e + 8 * g + 4 * hhe) = v2;
         *reinterpret_cast<u32x2*>(krow + 32 * e + 8 * g + 4 * hhe) = k2;
       }
@@ -343,11 +362,13 @@ hipError_t bwd_bf16_dkdv64(const BwdArgs& a) {
   if (a.causal)
     hipLaunchKernelGGL(bwd_kv64_kernel<true>, dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
-                       (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds);
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds,
+                       a.klen, a.heads);
   else
     hipLaunchKernelGGL(bwd_kv64_kernel<false>, dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
-                       (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds);
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds,
+                       a.klen, a.heads);
   return hipGetLastError();
 }
 

@@ -39,7 +39,8 @@ __device__ __forceinline__ float quad_sum(float x) {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
-                                                      float* __restrict__ LSE, int n, int nqb, float sl2e) {
+                                                      float* __restrict__ LSE, int n, int nqb, float sl2e,
+                                                      const int* __restrict__ klen, int heads) {
   constexpr int BQ = 16, BK = 64, NC = D / 16;  // NC: 4-float chunks per lane
   constexpr int PRE = BK * D / 4 / 256;         // 4-float chunks of a tile per thread (K, and V alike)
   __shared__ __attribute__((aligned(16))) float ks[BK * D];
@@ -60,7 +61,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     acc[i] = z;
   }
   float m = -INFINITY, l = 0.f;
-  const int kend = CAUSAL ? min(n, qb * BQ + BQ) : n;
+  const int nkv = padded_keys(klen, heads, bh, n);  // keys from nkv on are masked
+  const int kend = CAUSAL ? min(nkv, qb * BQ + BQ) : nkv;
   const int ntiles = (kend + BK - 1) / BK;
 
   // Thread tid stages chunks tid + 256 r of a tile (row = chunk / (D / 4)).
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
       }
       const float x = quad_sum(part) * sl2e;
       const int key = j0 + row;
-      const bool dead = key >= n || (CAUSAL && key > qrow);
+      const bool dead = key >= nkv || (CAUSAL && key > qrow);
       s[jj] = dead ? -INFINITY : x;
       mx = fmaxf(mx, s[jj]);
     }
@@ -150,15 +152,16 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     lw[u] = rm[(u * BQ + ql) * 2 + 1];
     mt = fmaxf(mt, mw[u]);
   }
-  // Key 0 (or, past the diagonal, the query's own key) is visible to every
-  // query, so mt is finite.
+  // Without key padding key 0 is visible to every query, so mt is finite; a
+  // row that sees no key (every key padded) gets O = 0 and LSE = -inf.
   float wt[4], lt = 0.f;
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     wt[u] = mw[u] == -INFINITY ? 0.f : fast_exp2(mw[u] - mt);
     lt += wt[u] * lw[u];
   }
-  const float inv = 1.0f / lt;
+  const bool empty = lt == 0.f;
+  const float inv = empty ? 0.f : 1.0f / lt;
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
@@ -172,7 +175,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
     for (int e = 0; e < 4; ++e) o[e] *= inv;
     *reinterpret_cast<f32x4*>(O + head + (size_t)qrow * D + 4 * (c + 4 * i)) = o;
   }
-  if (c == 0) LSE[(size_t)bh * n + qrow] = (mt + fast_log2(lt)) * kLn2;
+  if (c == 0) LSE[(size_t)bh * n + qrow] = empty ? -INFINITY : (mt + fast_log2(lt)) * kLn2;
 }
 
 // dK, dV for a block of 64 keys; streams query tiles of 32 rows.
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
                                                          const float* __restrict__ LSE,
                                                          const float* __restrict__ Dsum, float* __restrict__ dK,
                                                          float* __restrict__ dV, int n, int nkb, float scale,
-                                                         float sl2e) {
+                                                         float sl2e, const int* __restrict__ klen, int heads) {
   constexpr int BKEY = 64, BQ = 32, DQ = D / 4;
   __shared__ __attribute__((aligned(16))) float qs[BQ * D];
   __shared__ __attribute__((aligned(16))) float dos[BQ * D];
@@ -204,6 +207,7 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
     dk[i] = 0.f;
     dv[i] = 0.f;
   }
+  const int nkv = padded_keys(klen, heads, bh, n);  // keys from nkv on: P = 0, so dK = dV = 0
   const int istart = CAUSAL ? (kb * BKEY / BQ) * BQ : 0;
   for (int i0 = istart; i0 < n; i0 += BQ) {
     __syncthreads();
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
       }
       const float s = quad_sum(sp);
       const float dp = quad_sum(dpp);
-      const bool live = key < n && qi < n && (!CAUSAL || key <= qi);
+      const bool live = key < nkv && qi < n && (!CAUSAL || key <= qi);
       const float p = live ? fast_exp2(s * sl2e - lse2[ii]) : 0.f;
       const float ds = p * (dp - dsm[ii]);
 #pragma unroll
@@ -257,7 +261,8 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
                                                         const float* __restrict__ dO,
                                                         const float* __restrict__ LSE,
                                                         const float* __restrict__ Dsum, float* __restrict__ dQ,
-                                                        int n, int nqb, float scale, float sl2e) {
+                                                        int n, int nqb, float scale, float sl2e,
+                                                        const int* __restrict__ klen, int heads) {
   constexpr int BQ = 64, BKEY = 32, DQ = D / 4;
   __shared__ __attribute__((aligned(16))) float ks[BKEY * D];
   __shared__ __attribute__((aligned(16))) float vs[BKEY * D];
@@ -277,7 +282,8 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
   }
   const float l2 = qrow < n ? LSE[(size_t)bh * n + qrow] * kLog2e : 0.f;
   const float dsq = qrow < n ? Dsum[(size_t)bh * n + qrow] : 0.f;
-  const int kend = CAUSAL ? min(n, qb * BQ + BQ) : n;
+  const int nkv = padded_keys(klen, heads, bh, n);  // keys from nkv on are masked
+  const int kend = CAUSAL ? min(nkv, qb * BQ + BQ) : nkv;
   for (int j0 = 0; j0 < kend; j0 += BKEY) {
     __syncthreads();
     for (int idx = tid; idx < BKEY * D / 4; idx += 256) {
@@ -299,7 +305,7 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
       }
       const float s = quad_sum(sp);
       const float dp = quad_sum(dpp);
-      const bool live = kj < n && qrow < n && (!CAUSAL || kj <= qrow);
+      const bool live = kj < nkv && qrow < n && (!CAUSAL || kj <= qrow);
       const float p = live ? fast_exp2(s * sl2e - l2) : 0.f;
       const float ds = p * (dp - dsq);
 #pragma unroll
@@ -317,7 +323,7 @@ hipError_t fwd_f32_t(const FwdArgs& a) {
   const int nqb = (int)((a.n + 15) / 16);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqb)), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.n, nqb,
-                     a.scale * kLog2e);
+                     a.scale * kLog2e, a.klen, a.heads);
   return hipGetLastError();
 }
 
@@ -327,7 +333,7 @@ hipError_t dkdv_f32_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nkb)), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
                      (const float*)a.dsum, (float*)a.dk, (float*)a.dv, (int)a.n, nkb, a.scale,
-                     a.scale * kLog2e);
+                     a.scale * kLog2e, a.klen, a.heads);
   return hipGetLastError();
 }
 
@@ -336,7 +342,8 @@ hipError_t dq_f32_t(const BwdArgs& a) {
   const int nqb = (int)((a.n + 63) / 64);
   hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqb)), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
-                     (const float*)a.dsum, (float*)a.dq, (int)a.n, nqb, a.scale, a.scale * kLog2e);
+                     (const float*)a.dsum, (float*)a.dq, (int)a.n, nqb, a.scale, a.scale * kLog2e, a.klen,
+                     a.heads);
   return hipGetLastError();
 }
 

@@ -56,7 +56,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
                                                                    int total, float c, uint32_t qsign,
                                                                    const uint8_t* __restrict__ bmask,
                                                                    long long mask_stride, int nb, QkKernelArgs qa,
-                                                                   DropArgs dr) {
+                                                                   DropArgs dr, const int* __restrict__ klen,
+                                                                   int heads) {
   constexpr int BC = 64;               // keys per K/V tile
   constexpr int BU = 32;               // keys per pipeline unit (half a tile)
   constexpr int BR = NW * 32;          // query rows per workgroup
@@ -128,13 +129,15 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
     qf[s] = as_bf16x8(u);
   }
 
-  // Keys of this workgroup: [klo, khi) (its split; all keys when square),
-  // keys >= khi masked; causal (bottom-right when lengths differ: query i
+  // Keys of this workgroup: [klo, khi) (its split; all keys when square,
+  // or those below the padding), keys >= khi masked; causal (bottom-right when lengths differ: query i
   // sees key j when j <= i + coff) visits only up to kend.  Tiles jlo ..
   // ntiles - 1.
+  // Key padding (square lengths): keys from padded_keys(..) on are masked
+  // like keys past the end.
   const int coff = (QK && CAUSAL) ? qa.coff : 0;
   const int klo = QK ? sp * qa.kchunk : 0;
-  const int khi = QK ? min(nk, klo + qa.kchunk) : n;
+  const int khi = QK ? min(nk, klo + qa.kchunk) : padded_keys(klen, heads, bh, n);
   const int kend = CAUSAL ? min(khi, q0 + BR + coff) : khi;
   const int jlo = klo / BC;
   const int ntiles = kend > klo ? (kend + BC - 1) / BC : jlo;
@@ -455,7 +458,8 @@ static hipError_t launch_fwd(const FwdArgs& a) {
   }
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK, DROP>), dim3(total), dim3(NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb, qa, a.drop);
+                     (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb, qa, a.drop, a.klen,
+                     a.heads);
   return hipGetLastError();
 }
 

@@ -48,6 +48,11 @@ struct FwdArgs {
   float* lpart = nullptr;
   bool dropout = false;  // with `drop`
   DropArgs drop;
+  // Key padding (dense, square lengths): batch b = bh / heads attends only
+  // its keys j < klen[b] (device int32 [bh / heads], clamped to [0, n] by the
+  // kernels).  nullptr: every key.
+  const int* klen = nullptr;
+  int heads = 1;
 };
 
 // Kernel-side view of the unequal-length arguments.
@@ -93,7 +98,17 @@ struct BwdArgs {
   // dQ kernel and write it to `dsum`, instead of reading it from there; the
   // dK/dV launch then follows the dQ launch.
   bool dq_forms_dsum = false;
+  const int* klen = nullptr;  // as in FwdArgs
+  int heads = 1;
 };
+
+// Key count of (batch, head) bh under key padding: klen[bh / heads] clamped
+// to [0, n], or n without padding.
+__device__ __forceinline__ int padded_keys(const int* klen, int heads, int bh, int n) {
+  if (klen == nullptr) return n;
+  const int v = klen[bh / heads];
+  return v < 0 ? 0 : (v > n ? n : v);
+}
 
 // Block size of the block-sparse mask (query and key rows per block).
 constexpr int kSparseBlock = 128;

@@ -334,6 +334,40 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v,
                      float p_drop, uint64_t seed, uint64_t offset,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Key padding: the mask half of the element-wise operations that kernel
+ * fusion folds into the attention kernel ("Background", Paper Notes: mask
+ * listed beside dropout), in its most common form, a per-sequence key
+ * length.  For batch b, key j is masked (its score counts as -inf, as under
+ * the causal mask) when j >= key_len[b], for every head and query:
+ *
+ *   S_ij = -inf for j >= key_len[b] (and, with causal, for j > i),
+ *   P = softmax(S) per row, O = P V, LSE = log sum_j exp(S_ij),
+ *
+ * and the gradients are those of that masked softmax (textbook chain rule,
+ * as in attn_bwd); the padded keys' dK and dV are zero.  A row that sees no
+ * key (key_len[b] = 0) gets O = 0, LSE = -inf and dQ = 0.
+ *
+ * key_len: device int32 [B], read by the kernels (not validated on the
+ * host); a value below 0 counts as 0, above N as N.  NULL returns
+ * ATTN_E_NULL, a pointer not 4-byte aligned ATTN_E_ALIGN.  Square lengths,
+ * dense (no block mask, no dropout); both dtypes.  The padded rows of K and
+ * V must hold finite values (which ones does not change any result: they
+ * enter only with weight zero).  Other arguments, layout, ownership,
+ * workspace and errors as for attn_fwd / attn_bwd; the backward pass must be
+ * given the key_len (and causal, scale) of the forward.
+ */
+int attn_fwd_kpad(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                  int dtype, int causal, float scale, const int32_t* key_len,
+                  void* stream);
+
+int attn_bwd_kpad(const void* q, const void* k, const void* v, const void* o,
+                  const void* dout, const float* lse, void* dq, void* dk,
+                  void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                  int dtype, int causal, float scale, const int32_t* key_len,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);
 

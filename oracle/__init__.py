@@ -35,6 +35,8 @@ Modules:
 * :mod:`oracle.dropout` -- dropout on the probabilities (an element-wise op
   that "Background" on the Paper Notes page lists among those kernel fusion
   folds in), with the mask from the Philox4x32-10 counter-based generator.
+* :mod:`oracle.keypad` -- the key padding mask (the mask of that same list, as
+  per-sequence key lengths), with the conventions for rows that see no key.
 
 Every function here is pinned by ``tests/test_oracle*.py`` against page-printed
 values, closed forms, invariants, finite differences and a library autograd.

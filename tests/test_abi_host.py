@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
         "attn_bwd_dq_dsum",
         "attn_bwd_dropout",
         "attn_bwd_dsum",
+        "attn_bwd_kpad",
         "attn_bwd_noalloc",
         "attn_bwd_qk",
         "attn_bwd_qk_workspace_bytes",
@@ -41,6 +42,7 @@ def test_header_declares_the_boundary():
         "attn_fwd",
         "attn_fwd_blocksparse",
         "attn_fwd_dropout",
+        "attn_fwd_kpad",
         "attn_fwd_qk",
         "attn_fwd_qk_workspace_bytes",
         "attn_status_string",
@@ -331,3 +333,18 @@ def test_dropout_arguments_are_validated_before_any_launch():
     assert L.attn_bwd_dropout(*g, 1, 1, 16, 64, 0, 0, 0.1, 0.2, 1, 0, None, 1 << 20, None) == -5
     assert L.attn_bwd_dropout(*g, 1, 1, 16, 64, 0, 0, 0.1, 0.2, 1, 0, FAKE, 16, None) == -5
     assert E.attn_status_string(-7).startswith("dropout probability")
+
+
+def test_key_padding_arguments_are_validated_before_any_launch():
+    E, L = _lib()
+    f = [FAKE] * 5
+    # NULL key lengths, misaligned key lengths, bad shape, bad scale.
+    assert L.attn_fwd_kpad(*f, 1, 1, 16, 64, 0, 0, 0.1, None, None) == -1
+    assert L.attn_fwd_kpad(*f, 1, 1, 16, 64, 0, 0, 0.1, FAKE + 2, None) == -8
+    assert L.attn_fwd_kpad(*f, 1, 1, 16, 48, 0, 0, 0.1, FAKE, None) == -3
+    assert L.attn_fwd_kpad(*f, 1, 1, 16, 64, 0, 0, float("nan"), FAKE, None) == -4
+    g = [FAKE] * 9
+    assert L.attn_bwd_kpad(*g, 1, 1, 16, 64, 0, 0, 0.1, None, FAKE, 1 << 20, None) == -1
+    assert L.attn_bwd_kpad(*g, 1, 1, 16, 64, 0, 0, 0.1, FAKE + 2, FAKE, 1 << 20, None) == -8
+    assert L.attn_bwd_kpad(*g, 1, 1, 16, 64, 0, 0, 0.1, FAKE, None, 1 << 20, None) == -5
+    assert L.attn_bwd_kpad(*g, 1, 1, 16, 64, 0, 0, 0.1, FAKE, FAKE, 16, None) == -5
