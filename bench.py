@@ -308,6 +308,7 @@ def main():
     ap.add_argument("--blocksparse", action="store_true")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--dropout", action="store_true")
+    ap.add_argument("--window", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -353,6 +354,10 @@ def main():
 
     if args.dropout:
         dropout(torch, E, args.steps, args.warmup)
+        return
+
+    if args.window:
+        window(torch, E, args.steps, args.warmup)
         return
 
     shape = (4, 16, 4096, 128)
@@ -623,6 +628,46 @@ def dropout(torch, E, steps, warmup):
             "plain_fwd_ms": round(t_fwd, 4), "plain_bwd_ms": round(t_bwd, 4),
             "fwd_cost": round(t_fwd_d / t_fwd, 3), "bwd_cost": round(t_bwd_d / t_bwd, 3),
         }), flush=True)
+
+
+def window(torch, E, steps, warmup):
+    """Causal sliding window against the plain causal mask, bf16, d = 128:
+    forward and whole backward at N = 4096 (B=4 H=16) and N = 16384 (B=1
+    H=16) for windows of 256, 1024 and 4096 keys.  TFLOP/s count the products
+    of the attended (query, key) pairs only: 4 d per pair forward, 2.5 times
+    that backward."""
+    for shape in ((4, 16, 4096, 128), (1, 16, 16384, 128)):
+        b, h, n, d = shape
+        g = torch.Generator(device="cuda").manual_seed(19)
+        q, k, v, do = (torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16) for _ in range(4))
+        ws = torch.empty(max(E.attn_bwd_workspace_bytes(b, h, n, d, E.ATTN_BF16), 256), dtype=torch.uint8,
+                         device="cuda")
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+        o, lse = E.attn_fwd(q, k, v, causal=True)
+        t_fwd_c = _time_ms(torch, lambda: E.attn_fwd(q, k, v, causal=True, out=o, lse=lse), steps, warmup)
+        t_bwd_c = _time_ms(torch, lambda: E.attn_bwd(q, k, v, o, do, lse, causal=True, workspace=ws, grads=grads),
+                           steps, warmup)
+        for win in (256, 1024, 4096):
+            if win >= n:
+                continue
+            pairs = sum(min(i + 1, win) for i in range(n))
+            f = 4.0 * d * pairs * b * h
+            ow, lw = E.attn_fwd_window(q, k, v, win)
+            t_fwd = _time_ms(torch, lambda: E.attn_fwd_window(q, k, v, win, out=ow, lse=lw), steps, warmup)
+            t_bwd = _time_ms(torch, lambda: E.attn_bwd_window(q, k, v, ow, do, lw, win, workspace=ws, grads=grads),
+                             steps, warmup)
+            print(json.dumps({
+                "mode": "window", "B": b, "H": h, "N": n, "d": d, "window": win,
+                "fwd_ms": round(t_fwd, 4), "fwd_tflops": round(f / t_fwd / 1e9, 1),
+                "fwd_frac_peak": round(f / t_fwd / 1e9 / PEAK_BF16_TFLOPS, 4),
+                "bwd_ms": round(t_bwd, 4), "bwd_tflops": round(2.5 * f / t_bwd / 1e9, 1),
+                "bwd_frac_peak": round(2.5 * f / t_bwd / 1e9 / PEAK_BF16_TFLOPS, 4),
+                "causal_fwd_ms": round(t_fwd_c, 4), "causal_bwd_ms": round(t_bwd_c, 4),
+                "speedup_vs_causal": round((t_fwd_c + t_bwd_c) / (t_fwd + t_bwd), 3),
+                "pairs_ratio": round((n * (n + 1) / 2) / pairs, 3),
+            }), flush=True)
+        del q, k, v, do, ws, grads
+        torch.cuda.empty_cache()
 
 
 def decode(torch, E, steps, warmup):

@@ -19,6 +19,8 @@ Entry points carry the C names:
   on the probabilities (mask from a counter-based generator, not stored)
 * :func:`attn_fwd_kpad`, :func:`attn_bwd_kpad` -- the same with a key padding
   mask (per-sequence key lengths)
+* :func:`attn_fwd_window`, :func:`attn_bwd_window` -- causal attention over a
+  sliding window of the last ``window`` keys
 * :func:`attn_bwd_workspace_bytes`, :func:`attn_status_string`
 * :func:`lib` -- the raw ``ctypes.CDLL``.
 
@@ -46,6 +48,8 @@ __all__ = [
     "attn_bwd_dropout",
     "attn_fwd_kpad",
     "attn_bwd_kpad",
+    "attn_fwd_window",
+    "attn_bwd_window",
     "attn_bwd_workspace_bytes",
     "attn_status_string",
     "lib",
@@ -127,6 +131,11 @@ def lib():
     L.attn_bwd_kpad.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp, vp,
                                 ctypes.c_size_t, vp]
     L.attn_bwd_kpad.restype = i32
+    L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, f32, vp]
+    L.attn_fwd_window.restype = i32
+    L.attn_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i64, f32, vp,
+                                  ctypes.c_size_t, vp]
+    L.attn_bwd_window.restype = i32
     L.attn_status_string.argtypes = [i32]
     L.attn_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -588,4 +597,54 @@ def attn_bwd_kpad(q, k, v, o, do, lse, key_len, causal=False, scale=None, worksp
     )
     if st != 0:
         raise AttnError(st, "attn_bwd_kpad")
+    return dq, dk, dv
+
+
+def attn_fwd_window(q, k, v, window, scale=None, out=None, lse=None):
+    """Causal attention over a sliding window: query i attends keys
+    i - window < j <= i.  Returns (o, lse)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v)], q.shape, q.dtype, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check([("out", out)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    st = lib().attn_fwd_window(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, _dtype_code(q),
+        int(window), float(scale), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_fwd_window")
+    return out, lse
+
+
+def attn_bwd_window(q, k, v, o, do, lse, window, scale=None, workspace=None, grads=None):
+    """Backward of :func:`attn_fwd_window` (same window and scale); returns
+    (dq, dk, dv)."""
+    torch = _torch()
+    B, H, N, d = q.shape
+    _check([("q", q), ("k", k), ("v", v), ("o", o), ("do", do)], q.shape, q.dtype, q.device)
+    _check([("lse", lse)], (B, H, N), torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    code = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(B, H, N, d, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    _check([("dq", dq), ("dk", dk), ("dv", dv)], q.shape, q.dtype, q.device)
+    st = lib().attn_bwd_window(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(), dq.data_ptr(),
+        dk.data_ptr(), dv.data_ptr(), B, H, N, d, code, int(window), float(scale), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _stream_ptr(q.device),
+    )
+    if st != 0:
+        raise AttnError(st, "attn_bwd_window")
     return dq, dk, dv

@@ -187,7 +187,8 @@ const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_E_NULL: return "a required pointer is NULL";
-    case ATTN_E_SHAPE: return "invalid shape (B, H, N must be >= 1 and within size limits) or block-mask stride";
+    case ATTN_E_SHAPE:
+      return "invalid shape (B, H, N must be >= 1 and within size limits), block-mask stride or window (>= 1)";
     case ATTN_E_UNSUPPORTED: return "unsupported head dimension (64 or 128) or dtype (bf16 or fp32; block-sparse: bf16)";
     case ATTN_E_SCALE: return "scale must be finite";
     case ATTN_E_WORKSPACE: return "workspace missing or too small";
@@ -355,6 +356,50 @@ int attn_bwd_kpad(const void* q, const void* k, const void* v, const void* o, co
       make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, causal, scale, stream);
   a.klen = key_len;
   a.heads = (int)H;
+  return run_bwd(a, dtype == ATTN_BF16);
+}
+
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                    int64_t N, int64_t d, int dtype, int64_t window, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_E_NULL;
+  if (!all16(q, k, v, o) || !al4(lse)) return ATTN_E_ALIGN;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (window < 1) return ATTN_E_SHAPE;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.bh = B * H;
+  a.n = N;
+  a.d = d;
+  a.causal = true;
+  a.scale = scale;
+  a.stream = (hipStream_t)stream;
+  a.window = window < N ? (int)window : 0;  // a window of N keys or more is the causal mask
+  const hipError_t e = dtype == ATTN_BF16 ? attn::fwd_bf16(a) : attn::fwd_f32(a);
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                    int dtype, int64_t window, float scale, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_E_NULL;
+  if (!all16(q, k, v, o, dout, dq, dk, dv) || !al4(lse)) return ATTN_E_ALIGN;
+  const int st = check_shape(B, H, N, d, dtype);
+  if (st != ATTN_OK) return st;
+  if (window < 1) return ATTN_E_SHAPE;
+  if (!isfinite(scale)) return ATTN_E_SCALE;
+  if (!workspace || workspace_bytes < attn_bwd_workspace_bytes(B, H, N, d, dtype) ||
+      ((uintptr_t)workspace & 255) != 0)
+    return ATTN_E_WORKSPACE;
+  attn::BwdArgs a =
+      make_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, B, H, N, d, 1, scale, stream);
+  a.window = window < N ? (int)window : 0;
   return run_bwd(a, dtype == ATTN_BF16);
 }
 

@@ -100,7 +100,7 @@ __device__ __forceinline__ void pipeline_reads2() {
 template <int N>
 using int_c = std::integral_constant<int, N>;
 
-template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP>
+template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP, bool WIN = false>
 __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restrict__ Q,
                                                         const uint16_t* __restrict__ K,
                                                         const uint16_t* __restrict__ V,
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
                                                         int n, int nkb, int total, float scale, float sl2e,
                                                         const uint8_t* __restrict__ bmask, long long mask_stride,
                                                         int nk_arg, int coff_arg, DropArgs dr,
-                                                        const int* __restrict__ klen, int heads) {
+                                                        const int* __restrict__ klen, int heads, int wl) {
   constexpr int NW = 8, BKV = 128, BQ = 64;
   constexpr int TB = BQ * D * 2;  // bytes per 64-row tile
   constexpr int IPW = (D / 8) / NW;  // DMA loads per wave per tile
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
   // visits ntq - 2 kb of them) and there are half as many workgroup
   // hand-overs; otherwise one block, low key blocks (the most queries under
   // the causal mask) first.
-  constexpr bool PAIRED = CAUSAL && !SPARSE && !QK && !DROP;
+  constexpr bool PAIRED = CAUSAL && !SPARSE && !QK && !DROP && !WIN;
   const int lid = xcd_remap(blockIdx.x, total);
   const int nper = PAIRED ? (nkb + 1) / 2 : nkb;
   const int bh = lid / nper, kj = lid % nper;
@@ -215,11 +215,15 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[e][r] = 0.f;
 
-    const int ntq = (n + BQ - 1) / BQ;
+    // Query tiles it0 .. ntq - 1; under the sliding window (WIN: query i
+    // sees keys i - wl .. i) they end with the window of the block's last key.
+    const int ntq = WIN ? min((n + BQ - 1) / BQ, (k0 + BKV - 1 + wl) / BQ + 1) : (n + BQ - 1) / BQ;
     const int it0 = CAUSAL ? max(0, k0 - coff) / BQ : 0;
-    // A tile whose queries all precede this key group is skipped (causal);
-    // both waves of a pair decide alike.
-    auto active = [&](int i) ATTN_INLINE { return !CAUSAL || (i * BQ + BQ - 1 >= kw0 - coff); };
+    // A tile whose queries all precede this key group, or (WIN) all lie past
+    // its window, is skipped; both waves of a pair decide alike.
+    auto active = [&](int i) ATTN_INLINE {
+      return (!CAUSAL || (i * BQ + BQ - 1 >= kw0 - coff)) && (!WIN || i * BQ <= kw0 + 31 + wl);
+    };
 
     // Block-sparse: the query tiles whose mask block (a 64-row tile is half of
     // a 128-row block) may attend this key block (a workgroup's 128 keys are
@@ -481,6 +485,15 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
                 x[t][r] = key > q + coff ? -INFINITY : x[t][r];
               }
           }
+          if (WIN && i * BQ + BQ - 1 > kw0 + wl) {  // the window's far edge crosses the tile
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int q = i * BQ + 32 * t + crow(r, hh);
+                x[t][r] = q > key + wl ? -INFINITY : x[t][r];
+              }
+          }
 #pragma unroll
           for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -624,7 +637,7 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // dQ: query-stationary
 // ---------------------------------------------------------------------------
-template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP, bool WIN = false>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __restrict__ Q,
                                                            const uint16_t* __restrict__ K,
                                                            const uint16_t* __restrict__ V,
@@ -638,7 +651,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
                                                            int kchunk, float* __restrict__ dqpart,
                                                            const uint16_t* __restrict__ Osrc,
                                                            float* __restrict__ Dout,
-                                                           const int* __restrict__ klen, int heads) {
+                                                           const int* __restrict__ klen, int heads, int wl) {
   constexpr int BR = NW * 32, BC = 64;
 
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[BC * D];
@@ -739,9 +752,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   // are for tiles every key of which every row of the workgroup sees.
   auto compute = [&](const uint16_t* ks, const uint16_t* vs, int j0, auto tail) ATTN_INLINE {
     constexpr bool TAIL = decltype(tail)::value;
-    const bool active = !TAIL || !CAUSAL || (j0 <= wq0 + 31 + coff);
+    // (WIN: sliding window, query i sees keys i - wl .. i.)
+    const bool active = !TAIL || ((!CAUSAL || j0 <= wq0 + 31 + coff) && (!WIN || j0 + BC - 1 >= wq0 - wl));
     if (!active) return;
-    const bool need_mask = TAIL && ((j0 + BC > nk) || (CAUSAL && j0 + BC - 1 > wq0 + coff));
+    const bool need_mask =
+        TAIL && ((j0 + BC > nk) || (CAUSAL && j0 + BC - 1 > wq0 + coff) || (WIN && j0 < wq0 + 31 - wl));
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       // One half tile at a time: interleaving the halves costs more
@@ -792,7 +807,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kj = j0 + 32 * t + crow(r, hh);
-            x[r] = (kj >= nk || (CAUSAL && kj > qrow + coff)) ? -INFINITY : x[r];
+            x[r] = (kj >= nk || (CAUSAL && kj > qrow + coff) || (WIN && kj < qrow - wl)) ? -INFINITY : x[r];
           }
         }
 #pragma unroll
@@ -886,7 +901,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
     // with the checks.
     // (Under key padding a causal tile before the first row can still hold
     // padded keys: free tiles also lie wholly below nk.)
-    const int nfree = CAUSAL ? min(min(ntiles, nk / BC), max(0, (q0 + coff + 1) / BC)) : ntiles - 1;
+    // Under the sliding window the tiles start at the window of the first
+    // row, jlo, and every tile takes the checked path.
+    const int jlo = WIN ? max(0, q0 - wl) / BC : 0;
+    const int nfree =
+        WIN ? jlo : (CAUSAL ? min(min(ntiles, nk / BC), max(0, (q0 + coff + 1) / BC)) : ntiles - 1);
     auto fetch = [&](uint16_t* ks, uint16_t* vs, int jt) ATTN_INLINE {
       dma_tile<D, NW>(rk, ks, jt * BC, w, lane);
       dma_tile<D, NW>(rv, vs, jt * BC, w, lane);
@@ -895,9 +914,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
       wait_vmem();
       __syncthreads();
     };
-    fetch(k0s, v0s, 0);
+    fetch(k0s, v0s, jlo);
     settle();
-    int jt = 0;
+    int jt = jlo;
     for (; jt + 1 < nfree && jt + 2 < ntiles; jt += 2) {
       fetch(k1s, v1s, jt + 1);
       compute(k0s, v0s, jt * BC, std::false_type{});
@@ -972,19 +991,19 @@ __global__ __launch_bounds__(256) void dq_merge_kernel(const f32x4* __restrict__
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false>
+template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false, bool WIN = false>
 hipError_t launch_dkdv(const BwdArgs& a) {
   const int n = (int)a.n;
   const int nk = QK ? (int)a.nk : n;
   const int nkb = (nk + 127) / 128;
   // Causal, square, dense, no dropout: one workgroup per pair of mirrored
   // key blocks (see bwd_kv_kernel).
-  constexpr bool PAIRED = CAUSAL && !SPARSE && !QK && !DROP;
+  constexpr bool PAIRED = CAUSAL && !SPARSE && !QK && !DROP && !WIN;
   const int total = (int)(a.bh * (PAIRED ? (nkb + 1) / 2 : nkb));
-  hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, SPARSE, QK, DROP>), dim3(total), dim3(512), 0, a.stream,
+  hipLaunchKernelGGL((bwd_kv_kernel<D, CAUSAL, SPARSE, QK, DROP, WIN>), dim3(total), dim3(512), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout,
                      a.lse, a.dsum, (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e,
-                     a.bmask, (long long)a.mask_stride, nk, nk - n, a.drop, a.klen, a.heads);
+                     a.bmask, (long long)a.mask_stride, nk, nk - n, a.drop, a.klen, a.heads, a.window - 1);
   return hipGetLastError();
 }
 
@@ -992,7 +1011,7 @@ hipError_t launch_dkdv(const BwdArgs& a) {
 #define ATTN_DQ_NW128 8  // waves per dQ workgroup at d = 128 (tuning knob)
 #endif
 
-template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false>
+template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false, bool WIN = false>
 hipError_t launch_dq(const BwdArgs& a) {
   // Block-sparse: one mask block row per workgroup (4 waves), so that every
   // wave of a workgroup wants every tile the workgroup fetches.
@@ -1004,13 +1023,14 @@ hipError_t launch_dq(const BwdArgs& a) {
   const int nk = QK ? (int)a.nk : n;
   const bool split = QK && a.nsplit > 1;
   const bool form_d = a.dq_forms_dsum && !split;
-  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK, DROP>), dim3(total * (split ? a.nsplit : 1)),
+  hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK, DROP, WIN>), dim3(total * (split ? a.nsplit : 1)),
                      dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, form_d ? nullptr : a.dsum, (uint16_t*)a.dq, n, nqb, total,
                      a.scale,
                      a.scale * kLog2e, a.bmask, (long long)a.mask_stride, nb, nk, nk - n, a.drop,
                      split ? a.kchunk : 0, split ? a.dqpart : nullptr,
-                     form_d ? (const uint16_t*)a.o : nullptr, form_d ? a.dsum : nullptr, a.klen, a.heads);
+                     form_d ? (const uint16_t*)a.o : nullptr, form_d ? a.dsum : nullptr, a.klen, a.heads,
+                     a.window - 1);
   if (!split) return hipGetLastError();
   const long long n4 = a.bh * a.n * (long long)D / 4;
   const long long blocks = std::min<long long>((n4 + 255) / 256, 4096);
@@ -1034,6 +1054,8 @@ hipError_t dq_t(const BwdArgs& a) {
 }  // namespace
 
 hipError_t bwd_bf16_dkdv(const BwdArgs& a) {
+  if (a.window > 0)  // causal sliding window, dense, square lengths
+    return a.d == 64 ? bwd_bf16_dkdv64(a) : launch_dkdv<128, true, false, false, false, true>(a);
   if (a.dropout) {  // dense, square lengths only (checked by the caller)
     if (a.d == 64) return a.causal ? launch_dkdv<64, true, false, false, true>(a) : launch_dkdv<64, false, false, false, true>(a);
     return a.causal ? launch_dkdv<128, true, false, false, true>(a) : launch_dkdv<128, false, false, false, true>(a);
@@ -1047,6 +1069,8 @@ hipError_t bwd_bf16_dkdv(const BwdArgs& a) {
 int bwd_dq_rows(int64_t d) { return d == 128 ? 32 * ATTN_DQ_NW128 : 128; }
 
 hipError_t bwd_bf16_dq(const BwdArgs& a) {
+  if (a.window > 0)  // causal sliding window, dense, square lengths
+    return a.d == 64 ? launch_dq<64, true, false, false, false, true>(a) : launch_dq<128, true, false, false, false, true>(a);
   if (a.dropout) {
     if (a.d == 64) return a.causal ? launch_dq<64, true, false, false, true>(a) : launch_dq<64, false, false, false, true>(a);
     return a.causal ? launch_dq<128, true, false, false, true>(a) : launch_dq<128, false, false, false, true>(a);

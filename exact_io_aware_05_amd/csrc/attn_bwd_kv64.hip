@@ -75,7 +75,7 @@ __device__ __forceinline__ void dma_tile_at(const RsrcWords& rs, uint32_t lds, u
 #define ATTN_KV64_WAVES 3  // waves per SIMD the register budget is sized for (tuning knob)
 #endif
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool WIN = false>
 __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const uint16_t* __restrict__ Q,
                                                           const uint16_t* __restrict__ K,
                                                           const uint16_t* __restrict__ V,
@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
                                                           const float* __restrict__ Dsum, uint16_t* __restrict__ dK,
                                                           uint16_t* __restrict__ dV, int n, int nkb, int total,
                                                           float scale, float sl2e, float tau_ds,
-                                                          const int* __restrict__ klen, int heads) {
+                                                          const int* __restrict__ klen, int heads, int wl) {
   constexpr int D = 64, NW = 4, BKV = 32 * NW, BQ = 64;
   constexpr int TB = BQ * D * 2;     // bytes per 64-row tile
   constexpr int IPW = (D / 8) / NW;  // DMA loads per wave per tile
@@ -163,7 +163,9 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
       dka[e][r] = 0.f;
     }
 
-  const int ntq = (n + BQ - 1) / BQ;
+  // Query tiles it0 .. ntq - 1; under the sliding window (WIN: query i sees
+  // keys i - wl .. i) they end with the window of the block's last key.
+  const int ntq = WIN ? min((n + BQ - 1) / BQ, (k0 + BKV - 1 + wl) / BQ + 1) : (n + BQ - 1) / BQ;
   const int it0 = CAUSAL ? k0 / BQ : 0;
   const TileReader<D> TR(lane);
 
@@ -219,6 +221,7 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
     const float* dsr = dsm_at(b);
     const int q0 = i * BQ + 32 * t;
     if (CAUSAL && q0 + 31 < kw0) return;  // every query of the unit precedes every key of the wave
+    if (WIN && q0 > kw0 + 31 + wl) return;  // every query of the unit is past every key's window
     // dP starts from -D (its rows' values, in the registers' query order),
     // S from zero; both chains read their A operand rows from LDS.
     f32x16 cs, cp;
@@ -257,6 +260,15 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
       const int dq = q0 - kw0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) p[r] = lrel > dq + crow(r, 0) ? -INFINITY : p[r];
+    }
+    if (WIN && q0 + 31 > kw0 + wl) {
+      // query > key + wl  <=>  (q0 - kw0 - wl) + crow(r, 0) > l32 - 4 hh.
+      int lrel = threadIdx.x & 63;
+      asm volatile("" : "+v"(lrel));
+      lrel = (lrel & 31) - 4 * (lrel >> 5);
+      const int dw = q0 - kw0 - wl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = dw + crow(r, 0) > lrel ? -INFINITY : p[r];
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -359,16 +371,21 @@ hipError_t bwd_bf16_dkdv64(const BwdArgs& a) {
   // Split threshold of dS, which enters the products unscaled (the scale
   // multiplies dK at the end): a term's weight scale |dS| reaches 1/16.
   const float tau_ds = (1.0f / 16.0f) / fabsf(a.scale);
-  if (a.causal)
+  if (a.window > 0)
+    hipLaunchKernelGGL((bwd_kv64_kernel<true, true>), dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
+                       (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds,
+                       a.klen, a.heads, a.window - 1);
+  else if (a.causal)
     hipLaunchKernelGGL(bwd_kv64_kernel<true>, dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds,
-                       a.klen, a.heads);
+                       a.klen, a.heads, a.window - 1);
   else
     hipLaunchKernelGGL(bwd_kv64_kernel<false>, dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds,
-                       a.klen, a.heads);
+                       a.klen, a.heads, a.window - 1);
   return hipGetLastError();
 }
 

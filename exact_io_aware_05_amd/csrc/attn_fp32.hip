@@ -40,7 +40,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int n, int nqb, float sl2e,
-                                                      const int* __restrict__ klen, int heads) {
+                                                      const int* __restrict__ klen, int heads, int wl) {
   constexpr int BQ = 16, BK = 64, NC = D / 16;  // NC: 4-float chunks per lane
   constexpr int PRE = BK * D / 4 / 256;         // 4-float chunks of a tile per thread (K, and V alike)
   __shared__ __attribute__((aligned(16))) float ks[BK * D];
@@ -64,6 +64,10 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   const int nkv = padded_keys(klen, heads, bh, n);  // keys from nkv on are masked
   const int kend = CAUSAL ? min(nkv, qb * BQ + BQ) : nkv;
   const int ntiles = (kend + BK - 1) / BK;
+  // Sliding window (wl >= 0, with the causal mask): query i sees keys
+  // i - wl .. i; tiles before the window of the first query are skipped.
+  const bool win = wl >= 0;
+  const int t0 = win ? max(0, qb * BQ - wl) / BK : 0;
 
   // Thread tid stages chunks tid + 256 r of a tile (row = chunk / (D / 4)).
   f32x4 kn[PRE], vn[PRE];
@@ -76,8 +80,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
       vn[r] = key < n ? *reinterpret_cast<const f32x4*>(Vh + (size_t)key * D + 4 * c4) : z;
     }
   };
-  if (ntiles > 0) load(0);
-  for (int t = 0; t < ntiles; ++t) {
+  if (ntiles > t0) load(t0 * BK);
+  for (int t = t0; t < ntiles; ++t) {
     const int j0 = t * BK;
     __syncthreads();  // every wave is done with the previous tile
 #pragma unroll
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
       }
       const float x = quad_sum(part) * sl2e;
       const int key = j0 + row;
-      const bool dead = key >= nkv || (CAUSAL && key > qrow);
+      const bool dead = key >= nkv || (CAUSAL && key > qrow) || (win && key < qrow - wl);
       s[jj] = dead ? -INFINITY : x;
       mx = fmaxf(mx, s[jj]);
     }
@@ -186,7 +190,8 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
                                                          const float* __restrict__ LSE,
                                                          const float* __restrict__ Dsum, float* __restrict__ dK,
                                                          float* __restrict__ dV, int n, int nkb, float scale,
-                                                         float sl2e, const int* __restrict__ klen, int heads) {
+                                                         float sl2e, const int* __restrict__ klen, int heads,
+                                                         int wl) {
   constexpr int BKEY = 64, BQ = 32, DQ = D / 4;
   __shared__ __attribute__((aligned(16))) float qs[BQ * D];
   __shared__ __attribute__((aligned(16))) float dos[BQ * D];
@@ -209,7 +214,11 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
   }
   const int nkv = padded_keys(klen, heads, bh, n);  // keys from nkv on: P = 0, so dK = dV = 0
   const int istart = CAUSAL ? (kb * BKEY / BQ) * BQ : 0;
-  for (int i0 = istart; i0 < n; i0 += BQ) {
+  // Sliding window (wl >= 0): the block's keys are seen by queries up to
+  // its last key + wl.
+  const bool win = wl >= 0;
+  const int iend = win ? min(n, kb * BKEY + BKEY + wl) : n;
+  for (int i0 = istart; i0 < iend; i0 += BQ) {
     __syncthreads();
     for (int idx = tid; idx < BQ * D / 4; idx += 256) {
       const int row = idx / (D / 4), c4 = idx % (D / 4), qi = i0 + row;
@@ -235,7 +244,7 @@ __global__ __launch_bounds__(256) void bwd_kv_f32_kernel(const float* __restrict
       }
       const float s = quad_sum(sp);
       const float dp = quad_sum(dpp);
-      const bool live = key < nkv && qi < n && (!CAUSAL || key <= qi);
+      const bool live = key < nkv && qi < n && (!CAUSAL || key <= qi) && (!win || qi - key <= wl);
       const float p = live ? fast_exp2(s * sl2e - lse2[ii]) : 0.f;
       const float ds = p * (dp - dsm[ii]);
 #pragma unroll
@@ -262,7 +271,7 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
                                                         const float* __restrict__ LSE,
                                                         const float* __restrict__ Dsum, float* __restrict__ dQ,
                                                         int n, int nqb, float scale, float sl2e,
-                                                        const int* __restrict__ klen, int heads) {
+                                                        const int* __restrict__ klen, int heads, int wl) {
   constexpr int BQ = 64, BKEY = 32, DQ = D / 4;
   __shared__ __attribute__((aligned(16))) float ks[BKEY * D];
   __shared__ __attribute__((aligned(16))) float vs[BKEY * D];
@@ -284,7 +293,10 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
   const float dsq = qrow < n ? Dsum[(size_t)bh * n + qrow] : 0.f;
   const int nkv = padded_keys(klen, heads, bh, n);  // keys from nkv on are masked
   const int kend = CAUSAL ? min(nkv, qb * BQ + BQ) : nkv;
-  for (int j0 = 0; j0 < kend; j0 += BKEY) {
+  // Sliding window (wl >= 0): keys from the window of the block's first query.
+  const bool win = wl >= 0;
+  const int jstart = win ? max(0, qb * BQ - wl) / BKEY * BKEY : 0;
+  for (int j0 = jstart; j0 < kend; j0 += BKEY) {
     __syncthreads();
     for (int idx = tid; idx < BKEY * D / 4; idx += 256) {
       const int row = idx / (D / 4), c4 = idx % (D / 4), kj = j0 + row;
@@ -305,7 +317,7 @@ __global__ __launch_bounds__(256) void bwd_q_f32_kernel(const float* __restrict_
       }
       const float s = quad_sum(sp);
       const float dp = quad_sum(dpp);
-      const bool live = kj < nkv && qrow < n && (!CAUSAL || kj <= qrow);
+      const bool live = kj < nkv && qrow < n && (!CAUSAL || kj <= qrow) && (!win || qrow - kj <= wl);
       const float p = live ? fast_exp2(s * sl2e - l2) : 0.f;
       const float ds = p * (dp - dsq);
 #pragma unroll
@@ -323,7 +335,7 @@ hipError_t fwd_f32_t(const FwdArgs& a) {
   const int nqb = (int)((a.n + 15) / 16);
   hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqb)), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, (int)a.n, nqb,
-                     a.scale * kLog2e, a.klen, a.heads);
+                     a.scale * kLog2e, a.klen, a.heads, a.window - 1);
   return hipGetLastError();
 }
 
@@ -333,7 +345,7 @@ hipError_t dkdv_f32_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_kv_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nkb)), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
                      (const float*)a.dsum, (float*)a.dk, (float*)a.dv, (int)a.n, nkb, a.scale,
-                     a.scale * kLog2e, a.klen, a.heads);
+                     a.scale * kLog2e, a.klen, a.heads, a.window - 1);
   return hipGetLastError();
 }
 
@@ -343,7 +355,7 @@ hipError_t dq_f32_t(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_q_f32_kernel<D, CAUSAL>), dim3((unsigned)(a.bh * nqb)), dim3(256), 0, a.stream,
                      (const float*)a.q, (const float*)a.k, (const float*)a.v, (const float*)a.dout, a.lse,
                      (const float*)a.dsum, (float*)a.dq, (int)a.n, nqb, a.scale, a.scale * kLog2e, a.klen,
-                     a.heads);
+                     a.heads, a.window - 1);
   return hipGetLastError();
 }
 

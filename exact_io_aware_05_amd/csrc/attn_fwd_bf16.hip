@@ -47,7 +47,7 @@
 
 namespace attn {
 
-template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP, bool WIN = false>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __restrict__ Q,
                                                                    const uint16_t* __restrict__ K,
                                                                    const uint16_t* __restrict__ V,
@@ -57,7 +57,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
                                                                    const uint8_t* __restrict__ bmask,
                                                                    long long mask_stride, int nb, QkKernelArgs qa,
                                                                    DropArgs dr, const int* __restrict__ klen,
-                                                                   int heads) {
+                                                                   int heads, int wl) {
   constexpr int BC = 64;               // keys per K/V tile
   constexpr int BU = 32;               // keys per pipeline unit (half a tile)
   constexpr int BR = NW * 32;          // query rows per workgroup
@@ -135,8 +135,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   // ntiles - 1.
   // Key padding (square lengths): keys from padded_keys(..) on are masked
   // like keys past the end.
+  // Sliding window (WIN, with the causal mask): query i sees keys i - wl ..
+  // i, so the workgroup starts at key q0 - wl.
   const int coff = (QK && CAUSAL) ? qa.coff : 0;
-  const int klo = QK ? sp * qa.kchunk : 0;
+  const int klo = QK ? sp * qa.kchunk : (WIN ? max(0, q0 - wl) : 0);
   const int khi = QK ? min(nk, klo + qa.kchunk) : padded_keys(klen, heads, bh, n);
   const int kend = CAUSAL ? min(khi, q0 + BR + coff) : khi;
   const int jlo = klo / BC;
@@ -167,7 +169,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   };
   auto ju = [&](int u) ATTN_INLINE { return tile(u >> 1) * BC + BU * (u & 1); };  // first key of unit u
   auto active = [&](int j0) ATTN_INLINE { return !CAUSAL || j0 <= wq0 + 31 + coff; };
-  auto need_mask = [&](int j0) ATTN_INLINE { return j0 + BU > khi || (CAUSAL && j0 + BU - 1 > wq0 + coff); };
+  auto need_mask = [&](int j0) ATTN_INLINE {
+    return j0 + BU > khi || (CAUSAL && j0 + BU - 1 > wq0 + coff) || (WIN && j0 < wq0 + 31 - wl);
+  };
 
   // K of position p lives in ring slot p % R, V likewise.  Slots are
   // compile-time constants: SLOT = p mod R.
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j0 + crow(r, hh);
-          const bool dead = (key >= khi) || (CAUSAL && key > qrow + coff);
+          const bool dead = (key >= khi) || (CAUSAL && key > qrow + coff) || (WIN && key < qrow - wl);
           sc[r] = dead ? -INFINITY : sc[r];
         }
       }
@@ -434,7 +438,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   }
 }
 
-template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false>
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false, bool WIN = false>
 static hipError_t launch_fwd(const FwdArgs& a) {
   constexpr int BR = NW * 32;
   const int nqb = (int)((a.n + BR - 1) / BR);
@@ -456,10 +460,10 @@ static hipError_t launch_fwd(const FwdArgs& a) {
     qa.opart = a.opart;
     qa.lpart = a.lpart;
   }
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK, DROP>), dim3(total), dim3(NW * 64), 0, a.stream,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK, DROP, WIN>), dim3(total), dim3(NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb, qa, a.drop, a.klen,
-                     a.heads);
+                     a.heads, a.window - 1);
   return hipGetLastError();
 }
 
@@ -478,6 +482,10 @@ static hipError_t fwd_bf16_t(const FwdArgs& a) {
 }
 
 hipError_t fwd_bf16(const FwdArgs& a) {
+  if (a.window > 0) {  // causal sliding window, dense, square lengths
+    if (a.d == 64) return launch_fwd<64, 4, true, false, false, false, true>(a);
+    return launch_fwd<128, 8, true, false, false, false, true>(a);
+  }
   if (a.dropout) {
     // Dense, square lengths only (checked by the caller).
     if (a.d == 64)

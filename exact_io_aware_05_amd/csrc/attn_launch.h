@@ -53,6 +53,9 @@ struct FwdArgs {
   // kernels).  nullptr: every key.
   const int* klen = nullptr;
   int heads = 1;
+  // Causal sliding window (dense, square lengths): query i sees keys
+  // i - window + 1 .. i.  0: no window.
+  int window = 0;
 };
 
 // Kernel-side view of the unequal-length arguments.
@@ -100,6 +103,7 @@ struct BwdArgs {
   bool dq_forms_dsum = false;
   const int* klen = nullptr;  // as in FwdArgs
   int heads = 1;
+  int window = 0;  // as in FwdArgs
 };
 
 // Key count of (batch, head) bh under key padding: klen[bh / heads] clamped

@@ -368,6 +368,34 @@ int attn_bwd_kpad(const void* q, const void* k, const void* v, const void* o,
                   int dtype, int causal, float scale, const int32_t* key_len,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Causal sliding window (local attention): a second mask of the same kind,
+ * the causal mask restricted to the last `window` keys.  Query i attends
+ * keys j with i - window < j <= i:
+ *
+ *   S_ij = -inf unless i - window < j <= i,  P = softmax(S) per row,
+ *   O = P V, LSE = log sum_j exp(S_ij),
+ *
+ * with the gradients of that masked softmax (as in attn_bwd).  Every row sees
+ * at least its own key.  Key tiles wholly outside a query block's window are
+ * never visited, so the work grows as N * window rather than N^2 / 2.
+ * window >= N gives attn_fwd / attn_bwd's causal results bit for bit (the
+ * same kernels); window < 1 returns ATTN_E_SHAPE.  Square lengths, dense;
+ * both dtypes.  Other arguments, layout, ownership, workspace and errors as
+ * for attn_fwd / attn_bwd; the backward pass must be given the window (and
+ * scale) of the forward.
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o,
+                    float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                    int dtype, int64_t window, float scale, void* stream);
+
+int attn_bwd_window(const void* q, const void* k, const void* v,
+                    const void* o, const void* dout, const float* lse,
+                    void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                    int64_t N, int64_t d, int dtype, int64_t window,
+                    float scale, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);
 

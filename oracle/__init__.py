@@ -37,6 +37,8 @@ Modules:
   folds in), with the mask from the Philox4x32-10 counter-based generator.
 * :mod:`oracle.keypad` -- the key padding mask (the mask of that same list, as
   per-sequence key lengths), with the conventions for rows that see no key.
+* :mod:`oracle.window` -- the causal sliding-window mask (each query sees its
+  last ``window`` keys).
 
 Every function here is pinned by ``tests/test_oracle*.py`` against page-printed
 values, closed forms, invariants, finite differences and a library autograd.

@@ -38,6 +38,7 @@ def test_header_declares_the_boundary():
         "attn_bwd_noalloc",
         "attn_bwd_qk",
         "attn_bwd_qk_workspace_bytes",
+        "attn_bwd_window",
         "attn_bwd_workspace_bytes",
         "attn_fwd",
         "attn_fwd_blocksparse",
@@ -45,6 +46,7 @@ def test_header_declares_the_boundary():
         "attn_fwd_kpad",
         "attn_fwd_qk",
         "attn_fwd_qk_workspace_bytes",
+        "attn_fwd_window",
         "attn_status_string",
     ]
 
@@ -348,3 +350,18 @@ def test_key_padding_arguments_are_validated_before_any_launch():
     assert L.attn_bwd_kpad(*g, 1, 1, 16, 64, 0, 0, 0.1, FAKE + 2, FAKE, 1 << 20, None) == -8
     assert L.attn_bwd_kpad(*g, 1, 1, 16, 64, 0, 0, 0.1, FAKE, None, 1 << 20, None) == -5
     assert L.attn_bwd_kpad(*g, 1, 1, 16, 64, 0, 0, 0.1, FAKE, FAKE, 16, None) == -5
+
+
+def test_window_arguments_are_validated_before_any_launch():
+    E, L = _lib()
+    f = [FAKE] * 5
+    assert L.attn_fwd_window(None, *f[1:], 1, 1, 16, 64, 0, 4, 0.1, None) == -1
+    assert L.attn_fwd_window(*f, 1, 1, 16, 64, 0, 0, 0.1, None) == -2
+    assert L.attn_fwd_window(*f, 1, 1, 16, 64, 0, -3, 0.1, None) == -2
+    assert L.attn_fwd_window(*f, 1, 1, 16, 96, 0, 4, 0.1, None) == -3
+    assert L.attn_fwd_window(*f, 1, 1, 16, 64, 0, 4, float("inf"), None) == -4
+    g = [FAKE] * 9
+    assert L.attn_bwd_window(*g, 1, 1, 16, 64, 0, 0, 0.1, FAKE, 1 << 20, None) == -2
+    assert L.attn_bwd_window(*g, 1, 1, 16, 64, 0, 4, 0.1, None, 1 << 20, None) == -5
+    assert L.attn_bwd_window(*g, 1, 1, 16, 64, 0, 4, 0.1, FAKE, 16, None) == -5
+    assert "window" in E.attn_status_string(-2)
