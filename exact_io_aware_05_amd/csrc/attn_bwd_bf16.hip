@@ -651,7 +651,8 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
                                                            int kchunk, float* __restrict__ dqpart,
                                                            const uint16_t* __restrict__ Osrc,
                                                            float* __restrict__ Dout,
-                                                           const int* __restrict__ klen, int heads, int wl) {
+                                                           const int* __restrict__ klen, int heads, int wl,
+                                                           int hf_pass, int hf_fill) {
   constexpr int BR = NW * 32, BC = 64;
 
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[BC * D];
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
   // within each XCD.
   int bh, qi;
   if (CAUSAL) {
-    heavy_first(bid, total / nqb, nqb, bh, qi);
+    heavy_first(bid, total / nqb, nqb, bh, qi, hf_pass, hf_fill);
   } else {
     const int lid = xcd_remap(bid, total);
     bh = lid / nqb;
@@ -1026,6 +1027,8 @@ hipError_t launch_dq(const BwdArgs& a) {
   const int nk = QK ? (int)a.nk : n;
   const bool split = QK && a.nsplit > 1;
   const bool form_d = a.dq_forms_dsum && !split;
+  static int hf_pass = -1, hf_fill = 0;  // start-up placement of the causal order
+  if (hf_pass < 0) start_fill(bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK, DROP, WIN>, NW * 64, hf_pass, hf_fill);
   hipLaunchKernelGGL((bwd_q_kernel<D, NW, CAUSAL, SPARSE, QK, DROP, WIN>), dim3(total * (split ? a.nsplit : 1)),
                      dim3(NW * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                      (const uint16_t*)a.dout, a.lse, form_d ? nullptr : a.dsum, (uint16_t*)a.dq, n, nqb, total,
@@ -1033,7 +1036,7 @@ hipError_t launch_dq(const BwdArgs& a) {
                      a.scale * kLog2e, a.bmask, (long long)a.mask_stride, nb, nk, nk - n, a.drop,
                      split ? a.kchunk : 0, split ? a.dqpart : nullptr,
                      form_d ? (const uint16_t*)a.o : nullptr, form_d ? a.dsum : nullptr, a.klen, a.heads,
-                     a.window - 1);
+                     a.window - 1, split ? 0 : hf_pass, split ? 0 : hf_fill);
   if (!split) return hipGetLastError();
   const long long n4 = a.bh * a.n * (long long)D / 4;
   const long long blocks = std::min<long long>((n4 + 255) / 256, 4096);

@@ -84,7 +84,8 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
                                                           const float* __restrict__ Dsum, uint16_t* __restrict__ dK,
                                                           uint16_t* __restrict__ dV, int n, int nkb, int total,
                                                           float scale, float sl2e, float tau_ds,
-                                                          const int* __restrict__ klen, int heads, int wl) {
+                                                          const int* __restrict__ klen, int heads, int wl,
+                                                          int hf_pass, int hf_fill) {
   constexpr int D = 64, NW = 4, BKV = 32 * NW, BQ = 64;
   constexpr int TB = BQ * D * 2;     // bytes per 64-row tile
   constexpr int IPW = (D / 8) / NW;  // DMA loads per wave per tile
@@ -108,9 +109,16 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, l32 = lane & 31;
 
-  // Causal: low key blocks see the most queries; they come first.
-  const int lid = xcd_remap(blockIdx.x, total);
-  const int bh = lid / nkb, kb = lid % nkb;
+  // Causal: low key blocks see the most queries; they come first, longest
+  // first within each XCD (heavy_first, with the start-up placement).
+  int bh, kb;
+  if (CAUSAL) {
+    heavy_first(blockIdx.x, total / nkb, nkb, bh, kb, hf_pass, hf_fill);
+  } else {
+    const int lid = xcd_remap(blockIdx.x, total);
+    bh = lid / nkb;
+    kb = lid % nkb;
+  }
   const int k0 = kb * BKV;
   const int kw0 = k0 + 32 * w;
   const int key = kw0 + l32;
@@ -371,21 +379,25 @@ hipError_t bwd_bf16_dkdv64(const BwdArgs& a) {
   // Split threshold of dS, which enters the products unscaled (the scale
   // multiplies dK at the end): a term's weight scale |dS| reaches 1/16.
   const float tau_ds = (1.0f / 16.0f) / fabsf(a.scale);
+  static int hp[2] = {-1, -1}, hf[2] = {0, 0};  // start-up placement of the causal order
+  if (hp[0] < 0) start_fill(bwd_kv64_kernel<true, false>, 256, hp[0], hf[0]);
+  if (hp[1] < 0) start_fill(bwd_kv64_kernel<true, true>, 256, hp[1], hf[1]);
+  const int w = a.window > 0 ? 1 : 0;
   if (a.window > 0)
     hipLaunchKernelGGL((bwd_kv64_kernel<true, true>), dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds,
-                       a.klen, a.heads, a.window - 1);
+                       a.klen, a.heads, a.window - 1, hp[w], hf[w]);
   else if (a.causal)
     hipLaunchKernelGGL(bwd_kv64_kernel<true>, dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds,
-                       a.klen, a.heads, a.window - 1);
+                       a.klen, a.heads, a.window - 1, hp[w], hf[w]);
   else
     hipLaunchKernelGGL(bwd_kv64_kernel<false>, dim3(total), dim3(256), 0, a.stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.dsum,
                        (uint16_t*)a.dk, (uint16_t*)a.dv, n, nkb, total, a.scale, a.scale * kLog2e, tau_ds,
-                       a.klen, a.heads, a.window - 1);
+                       a.klen, a.heads, a.window - 1, hp[w], hf[w]);
   return hipGetLastError();
 }
 

@@ -192,7 +192,31 @@ __device__ __forceinline__ int xcd_remap(int pid, int total) {
 // the minimum but run 2-3% slower.
 // Every XCD receives exactly hx * nblk ids, so the map is a bijection of
 // [0, heads * nblk).  Otherwise the xcd_remap order (head-major) is kept.
-__device__ __forceinline__ void heavy_first(int pid, int heads, int nblk, int& bh, int& rank) {
+//
+// Several workgroups per CU (`fill` > `pass`): the first `fill` workgroups of
+// an XCD are placed at once, one slot of every CU per pass of `pass` (its CU
+// count), the k-th on CU k mod pass; so the blocks sharing a CU from the
+// start are those `pass` apart.  Then the XCD's heads are taken rank-major
+// (longest first over all of them) and, within the first fill, every odd
+// pass is reversed, so that a CU that starts with one of the heaviest blocks
+// of a pass also gets one of the lightest of the next (workgroups dispatched
+// later, into freed slots, keep the longest-first order).
+__device__ __forceinline__ void heavy_first(int pid, int heads, int nblk, int& bh, int& rank, int pass = 0,
+                                            int fill = 0) {
+  if ((heads & 7) == 0 && pass > 0 && fill > pass) {
+    const int hx = heads >> 3;
+    const int x = pid & 7, s = pid >> 3;
+    const int f = min(fill, hx * nblk);
+    int i = s;  // position in the XCD's longest-first list
+    if (s < f) {
+      const int p = s / pass, j = s - p * pass;
+      const int q = min(pass, f - p * pass);  // blocks in this pass
+      if (p & 1) i = p * pass + (q - 1 - j);
+    }
+    rank = i / hx;
+    bh = x * hx + (i - rank * hx);
+    return;
+  }
   if ((heads & 7) == 0) {
     const int hx = heads >> 3;
     const int x = pid & 7, s = pid >> 3;

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
                                                                    const uint8_t* __restrict__ bmask,
                                                                    long long mask_stride, int nb, QkKernelArgs qa,
                                                                    DropArgs dr, const int* __restrict__ klen,
-                                                                   int heads, int wl) {
+                                                                   int heads, int wl, int hf_pass, int hf_fill) {
   constexpr int BC = 64;               // keys per K/V tile
   constexpr int BU = 32;               // keys per pipeline unit (half a tile)
   constexpr int BR = NW * 32;          // query rows per workgroup
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
   const int nsplit = QK ? qa.nsplit : 1;
   int bh, qi, sp = 0;
   if (CAUSAL && nsplit == 1) {
-    heavy_first(blockIdx.x, total / nqb, nqb, bh, qi);
+    heavy_first(blockIdx.x, total / nqb, nqb, bh, qi, hf_pass, hf_fill);
   } else {
     const int lid = xcd_remap(blockIdx.x, total);
     const int per_head = nqb * nsplit;
@@ -474,10 +474,12 @@ static hipError_t launch_fwd(const FwdArgs& a) {
     qa.opart = a.opart;
     qa.lpart = a.lpart;
   }
+  static int hf_pass = -1, hf_fill = 0;  // start-up placement of the causal order
+  if (hf_pass < 0) start_fill(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK, DROP, WIN>, NW * 64, hf_pass, hf_fill);
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK, DROP, WIN>), dim3(total), dim3(NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb, qa, a.drop, a.klen,
-                     a.heads, a.window - 1);
+                     a.heads, a.window - 1, hf_pass, hf_fill);
   return hipGetLastError();
 }
 

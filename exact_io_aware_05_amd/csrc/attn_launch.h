@@ -106,6 +106,30 @@ struct BwdArgs {
   int window = 0;  // as in FwdArgs
 };
 
+// Compute units of the current device (cached after the first call).
+inline int device_cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
+// Start-up placement for heavy_first: pass = CUs per XCD, fill = pass times
+// the workgroups of `kernel` that fit on one CU at once (0, 0 when only one
+// does: nothing to balance at start).
+template <typename K>
+inline void start_fill(K kernel, int threads, int& pass, int& fill) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) per_cu = 1;
+  pass = device_cu_count() / 8;
+  fill = per_cu > 1 ? pass * per_cu : 0;
+  if (fill == 0) pass = 0;
+}
+
 // Key count of (batch, head) bh under key padding: klen[bh / heads] clamped
 // to [0, n], or n without padding.
 __device__ __forceinline__ int padded_keys(const int* klen, int heads, int bh, int n) {
