@@ -476,10 +476,16 @@ static hipError_t launch_fwd(const FwdArgs& a) {
   }
   static int hf_pass = -1, hf_fill = 0;  // start-up placement of the causal order
   if (hf_pass < 0) start_fill(fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK, DROP, WIN>, NW * 64, hf_pass, hf_fill);
+  // The forward takes the start-up placement only while most of its
+  // workgroups start at once (at most three start-up fills per XCD): with
+  // more, the rank-major order over all of an XCD's heads keeps too many keys
+  // and values in flight and the grouped order is faster (B=8 H=32 N=2048
+  // d=64 causal: 6%).
+  const bool place = (long long)total <= 3LL * 8 * hf_fill;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, SPARSE, QK, DROP, WIN>), dim3(total), dim3(NW * 64), 0, a.stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      (int)a.n, nqb, total, c, qsign, a.bmask, (long long)a.mask_stride, nb, qa, a.drop, a.klen,
-                     a.heads, a.window - 1, hf_pass, hf_fill);
+                     a.heads, a.window - 1, place ? hf_pass : 0, place ? hf_fill : 0);
   return hipGetLastError();
 }
 
