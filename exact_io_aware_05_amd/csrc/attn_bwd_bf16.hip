@@ -616,10 +616,39 @@ __global__ __launch_bounds__(512, 2) void bwd_kv_kernel(const uint16_t* __restri
       }
     }
 
-    if (key < nk) {
-      uint16_t* row = (s_role ? dV : dK) + khead + (size_t)key * D;
-      const float f = s_role ? 1.0f : scale;
-      const bool live = key < nkv;  // a padded key of a partly padded block: zero
+    const float f = s_role ? 1.0f : scale;
+    const bool live = key < nkv;  // a padded key of a partly padded block: zero
+    uint16_t* const out = s_role ? dV : dK;
+    if constexpr (D == 128) {
+      // dK and dV leave through LDS so that every store writes whole 128-byte
+      // row segments: each wave stages its 32 keys, 64 features at a time, in
+      // its own 4.5 KiB of the Q tile buffers (rows 144 bytes apart), once
+      // every wave is done with the tiles.
+      __syncthreads();
+      constexpr int RS = 72;  // row stride in bf16 elements
+      uint16_t* const stage = reinterpret_cast<uint16_t*>(smem + SMALL) + w * (32 * RS);
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int e = 2 * p + e2;
+            u32x2 o2;
+            o2[0] = pack_bf16x2(acc[e][4 * g + 0] * f, acc[e][4 * g + 1] * f);
+            o2[1] = pack_bf16x2(acc[e][4 * g + 2] * f, acc[e][4 * g + 3] * f);
+            if (!live) o2[0] = o2[1] = 0u;
+            *reinterpret_cast<u32x2*>(stage + l32 * RS + 32 * e2 + 8 * g + 4 * hh) = o2;
+          }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int r = 8 * k + (lane >> 3), c = lane & 7;
+          const u32x4 v4 = *reinterpret_cast<const u32x4*>(stage + r * RS + 8 * c);
+          if (kw0 + r < nk) *reinterpret_cast<u32x4*>(out + khead + (size_t)(kw0 + r) * D + 64 * p + 8 * c) = v4;
+        }
+      }
+    } else if (key < nk) {
+      uint16_t* row = out + khead + (size_t)key * D;
 #pragma unroll
       for (int e = 0; e < D / 32; ++e)
 #pragma unroll
@@ -958,6 +987,33 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
         for (int i = 0; i < 4; ++i) o4[i] = dqa[e][4 * g + i] * scale;
         *reinterpret_cast<f32x4*>(prow + 32 * e + 8 * g + 4 * hh) = o4;
       }
+  } else if (D == 128 && NW == 8 && !split) {
+    // dQ leaves through LDS so that every store writes whole 128-byte row
+    // segments (as the forward's O): each wave stages its 32 rows, 64
+    // features at a time, in a region of the tile buffers (rows 144 bytes
+    // apart), once every wave is done with the tiles.
+    __syncthreads();
+    constexpr int RS = 72;  // row stride in bf16 elements
+    uint16_t* const stage = (w < 3 ? k0s : w < 6 ? v0s : k1s) + (w % 3) * (32 * RS);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int e = 2 * p + e2;
+          u32x2 o2;
+          o2[0] = pack_bf16x2(dqa[e][4 * g + 0] * scale, dqa[e][4 * g + 1] * scale);
+          o2[1] = pack_bf16x2(dqa[e][4 * g + 2] * scale, dqa[e][4 * g + 3] * scale);
+          *reinterpret_cast<u32x2*>(stage + l32 * RS + 32 * e2 + 8 * g + 4 * hh) = o2;
+        }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int r = 8 * k + (lane >> 3), c = lane & 7;
+        const u32x4 v4 = *reinterpret_cast<const u32x4*>(stage + r * RS + 8 * c);
+        if (wq0 + r < n) *reinterpret_cast<u32x4*>(dQ + head + (size_t)(wq0 + r) * D + 64 * p + 8 * c) = v4;
+      }
+    }
   } else if (qrow < n) {
     uint16_t* drow = dQ + head + (size_t)qrow * D;
 #pragma unroll

@@ -130,3 +130,36 @@ def test_full_length_equals_plain_entry_points():
         assert torch.equal(o1, o2) and torch.equal(l1, l2)
         for a, b in zip(g1, g2):
             assert torch.equal(a, b)
+
+
+def test_key_padding_at_full_size():
+    """N = 4096, d = 128 (the forward's 256-row and the dK/dV kernel's 128-key
+    blocks, many of them wholly padded), every element against the oracle
+    (run per batch on the host cores)."""
+    from tests.gpu_util import oracle_map
+
+    shape, lens = (2, 1, 4096, 128), [2049, 1000]
+    E = _api()
+    scale = 1.0 / math.sqrt(128)
+    for causal in (False, True):
+        _announce("kpad full size", shape, lens, "causal" if causal else "full")
+        inp = _inputs(4343 + causal, shape, "bf16", lens)
+        q, k, v, do = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v", "do"))
+        key_len = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        o, lse = E.attn_fwd_kpad(q, k, v, key_len, causal=causal)
+        dq, dk, dv = E.attn_bwd_kpad(q, k, v, o, do, lse, key_len, causal=causal)
+        torch.cuda.synchronize()
+
+        def ref(b):
+            sl = {x: inp[x][b:b + 1] for x in ("q", "k", "v", "do")}
+            fo = KP.forward_keypad(sl["q"], sl["k"], sl["v"], lens[b:b + 1], causal, scale)
+            return fo, KP.backward_keypad(sl["q"], sl["k"], sl["v"], sl["do"], lens[b:b + 1], causal, scale)
+
+        refs = oracle_map(ref, range(shape[0]))
+        o_r = np.concatenate([r[0][0] for r in refs])
+        lse_r = np.concatenate([r[0][1] for r in refs])
+        g_r = [np.concatenate([r[1][i] for r in refs]) for i in range(3)]
+        assert_close(download(o), o_r, "bf16", "O")
+        _compare_lse(download(lse), lse_r, "bf16")
+        for name, got, ref_g in zip(("dQ", "dK", "dV"), (dq, dk, dv), g_r):
+            _close_rel(download(got), ref_g, "bf16", name)
