@@ -987,16 +987,21 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_q_kernel(const uint16_t* __res
         for (int i = 0; i < 4; ++i) o4[i] = dqa[e][4 * g + i] * scale;
         *reinterpret_cast<f32x4*>(prow + 32 * e + 8 * g + 4 * hh) = o4;
       }
-  } else if (D == 128 && NW == 8 && !split) {
+  } else if (!split) {
     // dQ leaves through LDS so that every store writes whole 128-byte row
     // segments (as the forward's O): each wave stages its 32 rows, 64
     // features at a time, in a region of the tile buffers (rows 144 bytes
-    // apart), once every wave is done with the tiles.
+    // apart; three regions per buffer at d = 128, one at d = 64), once every
+    // wave is done with the tiles.
     __syncthreads();
-    constexpr int RS = 72;  // row stride in bf16 elements
-    uint16_t* const stage = (w < 3 ? k0s : w < 6 ? v0s : k1s) + (w % 3) * (32 * RS);
+    constexpr int RS = 72;                                // row stride in bf16 elements
+    constexpr int PER = BC * D >= 3 * 32 * RS ? 3 : 1;  // regions per tile buffer
+    static_assert(NW <= 4 * PER, "the staging regions fit the tile buffers");
+    static_assert(BC * D >= 32 * RS, "a staging region fits a tile buffer");
+    const int ra = w / PER;
+    uint16_t* const stage = (ra == 0 ? k0s : ra == 1 ? v0s : ra == 2 ? k1s : v1s) + (w % PER) * (32 * RS);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < D / 64; ++p) {
 #pragma unroll
       for (int e2 = 0; e2 < 2; ++e2)
 #pragma unroll

@@ -350,22 +350,37 @@ __global__ __launch_bounds__(256, ATTN_KV64_WAVES) void bwd_kv64_kernel(const ui
   asm volatile("" : "+v"(le));
   const int keye = kw0 + (le & 31), hhe = le >> 5;
   const bool live = keye < nkv;  // a padded key of a partly padded block: zero
-  if (keye < n) {
-    uint16_t* vrow = dV + head + (size_t)keye * D;
-    uint16_t* krow = dK + head + (size_t)keye * D;
+  // dV and dK leave through LDS so that every store writes whole 128-byte
+  // rows: each wave stages its 32 keys of both (rows 144 bytes apart) in its
+  // own 9 KiB of the tile buffers, once every wave is done with the tiles,
+  // and reads them back 16 bytes per lane, eight rows per instruction.
+  __syncthreads();
+  constexpr int RS = 72;  // row stride in bf16 elements
+  uint16_t* const sv = reinterpret_cast<uint16_t*>(smem + SMALL) + w * (2 * 32 * RS);
+  uint16_t* const sk = sv + 32 * RS;
+  const int le32 = le & 31;
 #pragma unroll
-    for (int e = 0; e < D / 32; ++e)
+  for (int e = 0; e < D / 32; ++e)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 v2, k2;
-        v2[0] = pack_bf16x2(dva[e][4 * g + 0], dva[e][4 * g + 1]);
-        v2[1] = pack_bf16x2(dva[e][4 * g + 2], dva[e][4 * g + 3]);
-        k2[0] = pack_bf16x2(dka[e][4 * g + 0] * scale, dka[e][4 * g + 1] * scale);
-        k2[1] = pack_bf16x2(dka[e][4 * g + 2] * scale, dka[e][4 * g + 3] * scale);
-        if (!live) v2[0] = v2[1] = k2[0] = k2[1] = 0u;
-        *reinterpret_cast<u32x2*>(vrow + 32 * e + 8 * g + 4 * hhe) = v2;
-        *reinterpret_cast<u32x2*>(krow + 32 * e + 8 * g + 4 * hhe) = k2;
-      }
+    for (int g = 0; g < 4; ++g) {
+      u32x2 v2, k2;
+      v2[0] = pack_bf16x2(dva[e][4 * g + 0], dva[e][4 * g + 1]);
+      v2[1] = pack_bf16x2(dva[e][4 * g + 2], dva[e][4 * g + 3]);
+      k2[0] = pack_bf16x2(dka[e][4 * g + 0] * scale, dka[e][4 * g + 1] * scale);
+      k2[1] = pack_bf16x2(dka[e][4 * g + 2] * scale, dka[e][4 * g + 3] * scale);
+      if (!live) v2[0] = v2[1] = k2[0] = k2[1] = 0u;
+      *reinterpret_cast<u32x2*>(sv + le32 * RS + 32 * e + 8 * g + 4 * hhe) = v2;
+      *reinterpret_cast<u32x2*>(sk + le32 * RS + 32 * e + 8 * g + 4 * hhe) = k2;
+    }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = 8 * k + (le >> 3), c = le & 7;
+    const u32x4 v4 = *reinterpret_cast<const u32x4*>(sv + r * RS + 8 * c);
+    const u32x4 k4 = *reinterpret_cast<const u32x4*>(sk + r * RS + 8 * c);
+    if (kw0 + r < n) {
+      *reinterpret_cast<u32x4*>(dV + head + (size_t)(kw0 + r) * D + 8 * c) = v4;
+      *reinterpret_cast<u32x4*>(dK + head + (size_t)(kw0 + r) * D + 8 * c) = k4;
+    }
   }
 }
 

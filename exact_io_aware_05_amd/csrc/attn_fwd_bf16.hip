@@ -437,48 +437,41 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(const uint16_t* __
     }
     return;
   }
-  if constexpr (D == 128 && NW == 8) {
-    // O leaves through LDS so that every store writes whole 128-byte row
-    // segments: each wave stages its 32 rows, 64 features at a time, in a
-    // region of the K ring (rows 144 bytes apart), and reads them back 16
-    // bytes per lane, eight rows per instruction.  The ring is free once
-    // every wave has passed this barrier.
-    __syncthreads();
-    constexpr int RS = 72;  // row stride in bf16 elements (144 bytes)
-    uint16_t* const stage = (w < 3 ? k0s : w < 6 ? k1s : k2s) + (w % 3) * (32 * RS);
+  // O leaves through LDS so that every store writes whole 128-byte row
+  // segments: each wave stages its 32 rows, 64 features at a time, in a
+  // region of the ring (rows 144 bytes apart; three regions per slot at
+  // d = 128, one at d = 64), and reads them back 16 bytes per lane, eight
+  // rows per instruction.  The ring is free once every wave has passed this
+  // barrier.
+  __syncthreads();
+  constexpr int RS = 72;                           // row stride in bf16 elements (144 bytes)
+  constexpr int PER = TB >= 3 * 32 * RS ? 3 : 1;  // regions per ring slot
+  static_assert(NW <= PER * (R > 2 ? 3 : 4), "the staging regions fit the ring");
+  static_assert(TB >= 32 * RS, "a staging region fits a ring slot");
+  const int ra = w / PER;
+  uint16_t* const base = R > 2 ? (ra == 0 ? k0s : ra == 1 ? k1s : k2s)
+                               : (ra == 0 ? k0s : ra == 1 ? k1s : ra == 2 ? v0s : v1s);
+  uint16_t* const stage = base + (w % PER) * (32 * RS);
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+  for (int p = 0; p < D / 64; ++p) {
 #pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int e = 2 * p + e2;
-          u32x2 o2;
-          o2[0] = pack_bf16x2(oacc[e][4 * g + 0] * inv, oacc[e][4 * g + 1] * inv);
-          o2[1] = pack_bf16x2(oacc[e][4 * g + 2] * inv, oacc[e][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>(stage + l32 * RS + 32 * e2 + 8 * g + 4 * hh) = o2;
-        }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int r = 8 * k + (lane >> 3), c = lane & 7;
-        const u32x4 v4 = *reinterpret_cast<const u32x4*>(stage + r * RS + 8 * c);
-        if (wq0 + r < n) *reinterpret_cast<u32x4*>(O + head + (size_t)(wq0 + r) * D + 64 * p + 8 * c) = v4;
-      }
-    }
-    if (qrow < n && hh == 0) LSE[(size_t)bh * n + qrow] = lse_v;
-  } else if (qrow < n) {
-    uint16_t* orow = O + head + (size_t)qrow * D;
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e)
+    for (int e2 = 0; e2 < 2; ++e2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        const int e = 2 * p + e2;
         u32x2 o2;
         o2[0] = pack_bf16x2(oacc[e][4 * g + 0] * inv, oacc[e][4 * g + 1] * inv);
         o2[1] = pack_bf16x2(oacc[e][4 * g + 2] * inv, oacc[e][4 * g + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + 32 * e + 8 * g + 4 * hh) = o2;
+        *reinterpret_cast<u32x2*>(stage + l32 * RS + 32 * e2 + 8 * g + 4 * hh) = o2;
       }
-    if (hh == 0) LSE[(size_t)bh * n + qrow] = lse_v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int r = 8 * k + (lane >> 3), c = lane & 7;
+      const u32x4 v4 = *reinterpret_cast<const u32x4*>(stage + r * RS + 8 * c);
+      if (wq0 + r < n) *reinterpret_cast<u32x4*>(O + head + (size_t)(wq0 + r) * D + 64 * p + 8 * c) = v4;
+    }
   }
+  if (qrow < n && hh == 0) LSE[(size_t)bh * n + qrow] = lse_v;
 }
 
 template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false, bool WIN = false>
