@@ -309,6 +309,7 @@ def main():
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--dropout", action="store_true")
     ap.add_argument("--window", action="store_true")
+    ap.add_argument("--probes", action="store_true", help="diagnostic microbenchmarks (libattn_probe.so)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -342,6 +343,10 @@ def main():
 
     if args.sweep:
         sweep(torch, E, args.steps, args.warmup)
+        return
+
+    if args.probes:
+        probes(torch)
         return
 
     if args.blocksparse:
@@ -437,6 +442,34 @@ def main():
 
 
 PEAK_FP32_TFLOPS = 157.3
+
+
+def probes(torch):
+    """Diagnostic microbenchmarks, one JSON line each: fp32 atomic adds of a dQ
+    accumulated by key blocks (and plain stores of the same tiles) at the
+    B=8 H=16 N=2048 d=64 and B=4 H=16 N=4096 d=128 shapes, the instruction-mix
+    cycles at one and two waves per SIMD, and the MFMA rate and clock under
+    load."""
+    from exact_io_aware_05_amd import diag
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for d, heads, n in ((64, 128, 2048), (128, 64, 4096)):
+        for causal in (True, False):
+            for atomic in (True, False):
+                r = diag.atomic_dq(d, heads, n, causal, atomic)
+                print(json.dumps({"probe": "atomic_dq", "d": d, "heads": heads, "n": n, "causal": causal,
+                                  "op": "fp32 atomic add" if atomic else "plain store",
+                                  "ms": round(r["ms"], 4), "GB_per_s": round(r["GB_per_s"], 1),
+                                  "bytes": r["bytes"], "mismatches": r["mismatches"]}), flush=True)
+    for waves in (1, 2):
+        for mix, name in diag.MIXES.items():
+            r = diag.issue_mix(mix, waves, cus)
+            print(json.dumps({"probe": "issue_mix", "mix": name, "waves_per_simd": waves,
+                              "mean_cycles_per_iter": round(r["mean_cycles"], 1),
+                              "max_cycles_per_iter": round(r["max_cycles"], 1)}), flush=True)
+    r = diag.mfma_rate(cus)
+    print(json.dumps({"probe": "mfma_rate", "cus": cus, "tflops": round(r["tflops"], 1), "ghz": round(r["ghz"], 3),
+                      "frac_of_2516.6": round(r["tflops"] / 2516.6, 3)}), flush=True)
 
 
 def _upload(torch, inp, dtype):

@@ -86,6 +86,14 @@ def lib():
             f"{LIB_PATH} is not built; run `python -m exact_io_aware_05_amd.build` "
             "(or __graft_entry__.build())"
         )
+    # torch ships its own HIP runtime under the system's soname; with torch
+    # loaded first the library binds to that one runtime, and device memory
+    # and streams from torch are valid in it (a second runtime loaded beside
+    # it would see no GPU once the first holds it).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, f32, vp]

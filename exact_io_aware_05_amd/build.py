@@ -1,10 +1,12 @@
-"""Build the HIP attention library (``libattn.so``) for gfx950 with hipcc, and
-the CPU library (``libattn_cpu.so``) with g++.
+"""Build the HIP attention library (``libattn.so``) for gfx950 with hipcc, the
+CPU library (``libattn_cpu.so``) with g++, and the diagnostic microbenchmarks
+(``libattn_probe.so``, not part of the attention library).
 
 Run as ``python -m exact_io_aware_05_amd.build``.  Each ``csrc/*.hip`` file is
 compiled to an object in ``_build/`` (in parallel), then linked in-tree to
 ``exact_io_aware_05_amd/libattn.so``; ``csrc/attn_cpu.cpp`` becomes
-``exact_io_aware_05_amd/libattn_cpu.so``.
+``exact_io_aware_05_amd/libattn_cpu.so`` and ``probe/attn_probe.hip``
+``exact_io_aware_05_amd/libattn_probe.so``.
 """
 
 import concurrent.futures
@@ -57,6 +59,21 @@ def build_cpu():
     return CPU_LIB
 
 
+PROBE_LIB = os.path.join(PKG, "libattn_probe.so")
+
+
+def build_probe():
+    """Compile probe/attn_probe.hip into exact_io_aware_05_amd/libattn_probe.so."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, os.path.join(PKG, "probe", "attn_probe.hip"), "-shared", "-o", tmp] + COMMON
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        err = "\n".join(line for line in (r.stderr or "").splitlines() if "packed-fp32-ops" not in line)
+        raise RuntimeError(f"hipcc failed for attn_probe.hip:\n{err}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
     cmd = [HIPCC, "-c", src, "-o", obj] + COMMON
@@ -85,6 +102,7 @@ def build(verbose=False):
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
     build_cpu()
+    build_probe()
     return LIB
 
 

@@ -1,0 +1,56 @@
+"""The diagnostic microbenchmark library (libattn_probe.so): it loads and
+exports its entry points, rejects bad sizes on the host, and (on a GPU) its
+atomic-add probe ends with exact counts and its timing probes return sane
+figures."""
+
+import ctypes
+import os
+
+import pytest
+
+from exact_io_aware_05_amd import diag
+
+
+def test_probe_library_exports():
+    L = diag.lib()
+    for name in ("probe_atomic_dq", "probe_issue_mix", "probe_mfma_rate"):
+        assert hasattr(L, name), name
+
+
+def test_probe_rejects_bad_sizes_on_the_host():
+    L = diag.lib()
+    ms, bad = ctypes.c_float(), ctypes.c_longlong()
+    assert L.probe_atomic_dq(64, 7, 256, 0, 1, 1, ctypes.byref(ms), ctypes.byref(bad)) != 0  # heads % 8
+    assert L.probe_atomic_dq(64, 8, 200, 0, 1, 1, ctypes.byref(ms), ctypes.byref(bad)) != 0  # n % 128
+    assert L.probe_atomic_dq(96, 8, 256, 0, 1, 1, ctypes.byref(ms), ctypes.byref(bad)) != 0  # d
+    mean, mx = ctypes.c_double(), ctypes.c_double()
+    assert L.probe_issue_mix(10, 1, 256, ctypes.byref(mean), ctypes.byref(mx)) != 0
+    assert L.probe_issue_mix(0, 3, 256, ctypes.byref(mean), ctypes.byref(mx)) != 0
+    tf, ghz = ctypes.c_double(), ctypes.c_double()
+    assert L.probe_mfma_rate(0, 10, ctypes.byref(tf), ctypes.byref(ghz)) != 0
+
+
+@pytest.fixture(scope="module")
+def cus():
+    import torch
+
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_atomic_probe_counts_are_exact(cus, d, causal):
+    print(f"atomic probe d={d} causal={causal}", flush=True)
+    for atomic in (True, False):
+        r = diag.atomic_dq(d, 8, 256, causal, atomic, reps=3)
+        assert r["mismatches"] == 0
+        assert r["ms"] > 0
+
+
+@pytest.mark.gpu
+def test_issue_and_rate_probes(cus):
+    r = diag.issue_mix(0, 1, cus)  # 16 MFMA of 32 cycles each
+    assert 400 < r["max_cycles"] < 800
+    r = diag.mfma_rate(cus, iters=2000)
+    assert r["tflops"] > 0 and 0.5 < r["ghz"] < 4.0
