@@ -54,3 +54,25 @@ def test_issue_and_rate_probes(cus):
     assert 400 < r["max_cycles"] < 800
     r = diag.mfma_rate(cus, iters=2000)
     assert r["tflops"] > 0 and 0.5 < r["ghz"] < 4.0
+
+
+def test_bindings_load_torch_before_their_hip_library():
+    """Both ctypes bindings import torch before loading a HIP library, so the
+    library binds to torch's HIP runtime (same soname) instead of loading the
+    system runtime beside it, which would see no GPU once torch's holds it."""
+    import subprocess
+    import sys
+
+    code = (
+        "import sys\n"
+        "import exact_io_aware_05_amd as E\n"
+        "from exact_io_aware_05_amd import diag\n"
+        "assert 'torch' not in sys.modules\n"
+        "E.lib()\n"
+        "assert 'torch' in sys.modules\n"
+        "diag.lib()\n"
+        "print('ok')\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
