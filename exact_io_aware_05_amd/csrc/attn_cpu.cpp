@@ -11,15 +11,19 @@
 // OpenMP spreads the work items over the cores.
 //
 // Every product has the form C[i][0:w] += sum_k a(i, k) B[k][0:w] with B and
-// C rows contiguous (a tile transposed once where needed), computed 64
-// columns at a time in eight 8-float vector accumulators, so the compiler
-// emits packed FMAs (AVX2) whatever the leading dimensions.
+// C rows contiguous (a tile transposed once where needed).  Four rows of C
+// share each load of a B row segment: 4 x 16 columns in eight 8-float
+// accumulators (AVX2), or 4 x 64 columns in sixteen 16-float accumulators
+// (AVX-512, chosen at run time where the host has it; ATTN_CPU_ISA=avx2 forces
+// the 8-float form).  Each element still adds its k terms in order, one fused
+// multiply-add each, so both forms give the same results.
 #include "attn_cpu.h"
 
 #include <omp.h>
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -31,6 +35,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef float v8f __attribute__((vector_size(32)));
+typedef float v16f __attribute__((vector_size(64)));
 
 // 2^x in float32 for the softmax: x = n + f with n = round(x), |f| <= 1/2;
 // 2^f = exp(f ln 2) by its Taylor series to degree 7 (coefficients
@@ -57,30 +62,78 @@ inline float exp2_sm(float x) {
   return p * s;
 }
 
-// C[i][0:w] += sum_{k < kd} a(i, k) * B[k][0:w] for i < m, with
-// a(i, k) = A[i * ai + k * ak]; w a multiple of 64; B, C row strides ldb, ldc.
-// One row by 64 columns at a time: eight 8-float accumulators in registers.
-inline void axpy_rows(int m, int kd, const float* A, int ai, int ak, const float* B, int ldb, float* C, int ldc,
-                      int w) {
-  for (int c0 = 0; c0 < w; c0 += 64) {
-    for (int i = 0; i < m; ++i) {
-      v8f acc[8];
-      float* crow = C + (size_t)i * ldc + c0;
-      for (int t = 0; t < 8; ++t) std::memcpy(&acc[t], crow + 8 * t, 32);
-      const float* arow = A + (size_t)i * ai;
-      for (int k = 0; k < kd; ++k) {
-        const float s = arow[(size_t)k * ak];
-        const v8f sv = {s, s, s, s, s, s, s, s};
-        const float* b = B + (size_t)k * ldb + c0;
-        for (int t = 0; t < 8; ++t) {
-          v8f bv;
-          std::memcpy(&bv, b + 8 * t, 32);
-          acc[t] += sv * bv;
-        }
-      }
-      for (int t = 0; t < 8; ++t) std::memcpy(crow + 8 * t, &acc[t], 32);
+// Rows i0 .. i0 + RB - 1 of C, columns c0 .. c0 + NV * lanes(V) - 1:
+// C[i][c] += sum_{k < kd} a(i, k) * B[k][c], a(i, k) = A[i * ai + k * ak].
+// The accumulators stay in registers; every B row segment is loaded once for
+// the RB rows.
+template <typename V, int NV, int RB>
+__attribute__((always_inline)) inline void axpy_block(int kd, const float* A, int ai, int ak, const float* B, int ldb,
+                                                      float* C, int ldc, int i0, int c0) {
+  constexpr int VW = (int)(sizeof(V) / sizeof(float));
+  V acc[RB][NV];
+#pragma GCC unroll 8
+  for (int r = 0; r < RB; ++r)
+#pragma GCC unroll 8
+    for (int t = 0; t < NV; ++t) std::memcpy(&acc[r][t], C + (size_t)(i0 + r) * ldc + c0 + VW * t, sizeof(V));
+  for (int k = 0; k < kd; ++k) {
+    const float* b = B + (size_t)k * ldb + c0;
+    V bv[NV];
+#pragma GCC unroll 8
+    for (int t = 0; t < NV; ++t) std::memcpy(&bv[t], b + VW * t, sizeof(V));
+#pragma GCC unroll 8
+    for (int r = 0; r < RB; ++r) {
+      const V sv = V{} + A[(size_t)(i0 + r) * ai + (size_t)k * ak];
+#pragma GCC unroll 8
+      for (int t = 0; t < NV; ++t) acc[r][t] += sv * bv[t];
     }
   }
+#pragma GCC unroll 8
+  for (int r = 0; r < RB; ++r)
+#pragma GCC unroll 8
+    for (int t = 0; t < NV; ++t) std::memcpy(C + (size_t)(i0 + r) * ldc + c0 + VW * t, &acc[r][t], sizeof(V));
+}
+
+// C[i][0:w] += sum_{k < kd} a(i, k) * B[k][0:w] for i < m (w a multiple of
+// 64; B, C row strides ldb, ldc): blocks of four rows, then single rows.
+template <typename V, int NV>
+__attribute__((always_inline)) inline void axpy_rows_v(int m, int kd, const float* A, int ai, int ak, const float* B,
+                                                       int ldb, float* C, int ldc, int w) {
+  constexpr int CW = NV * (int)(sizeof(V) / sizeof(float));
+  for (int c0 = 0; c0 < w; c0 += CW) {
+    int i = 0;
+    for (; i + 4 <= m; i += 4) axpy_block<V, NV, 4>(kd, A, ai, ak, B, ldb, C, ldc, i, c0);
+    for (; i < m; ++i) axpy_block<V, NV, 1>(kd, A, ai, ak, B, ldb, C, ldc, i, c0);
+  }
+}
+
+void axpy_rows_avx2(int m, int kd, const float* A, int ai, int ak, const float* B, int ldb, float* C, int ldc,
+                    int w) {
+  axpy_rows_v<v8f, 2>(m, kd, A, ai, ak, B, ldb, C, ldc, w);
+}
+
+__attribute__((target("avx512f"))) void axpy_rows_avx512(int m, int kd, const float* A, int ai, int ak,
+                                                          const float* B, int ldb, float* C, int ldc, int w) {
+  axpy_rows_v<v16f, 4>(m, kd, A, ai, ak, B, ldb, C, ldc, w);
+}
+
+// The 16-float form where the host has AVX-512 (and ATTN_CPU_ISA does not
+// ask for avx2).
+bool use_avx512() {
+  static const bool wide = [] {
+    const char* isa = std::getenv("ATTN_CPU_ISA");
+    if (isa != nullptr && std::strcmp(isa, "avx2") == 0) return false;
+    __builtin_cpu_init();
+    return __builtin_cpu_supports("avx512f") != 0;
+  }();
+  return wide;
+}
+
+inline void axpy_rows(int m, int kd, const float* A, int ai, int ak, const float* B, int ldb, float* C, int ldc,
+                      int w) {
+  if (use_avx512())
+    axpy_rows_avx512(m, kd, A, ai, ak, B, ldb, C, ldc, w);
+  else
+    axpy_rows_avx2(m, kd, A, ai, ak, B, ldb, C, ldc, w);
 }
 
 // Rows [r0, r0 + rows) of a [n, d] matrix, transposed into T[dd][BK] (keys

@@ -100,3 +100,41 @@ def test_invalid_arguments_are_rejected():
     assert L.attn_cpu_fwd(p, p, p, p, p, 1, 1, 16, 64, 0, float("nan"), 1) == -4
     assert L.attn_cpu_bwd(p, p, p, p, p, p, p, p, None, 1, 1, 16, 64, 0, 0.1, 1) == -1
     assert L.attn_cpu_bwd(p, p, p, p, p, p, p, p, p, 1, 1, 0, 64, 0, 0.1, 1) == -2
+
+
+def test_vector_paths_give_identical_results():
+    """The library's products run in 16-float (AVX-512, where the host has it)
+    or 8-float vectors; each output element adds the same terms in the same
+    order either way, so the two paths must agree bit for bit.  The 8-float
+    path runs in a child process with ATTN_CPU_ISA=avx2."""
+    import subprocess
+    import sys
+
+    C = _cpu()
+    shape = (1, 2, 150, 64)
+    inp = synth.qkvdo(77, shape, "bf16")
+    scale = 1.0 / math.sqrt(shape[3])
+    o, lse = C.attn_cpu_fwd(inp["q"], inp["k"], inp["v"], True, scale)
+    dq, dk, dv = C.attn_cpu_bwd(inp["q"], inp["k"], inp["v"], o, inp["do"], lse, True, scale)
+    code = (
+        "import sys, math, numpy as np\n"
+        "import synth\n"
+        "from exact_io_aware_05_amd import cpu as C\n"
+        "inp = synth.qkvdo(77, (1, 2, 150, 64), 'bf16')\n"
+        "s = 1.0 / math.sqrt(64)\n"
+        "o, lse = C.attn_cpu_fwd(inp['q'], inp['k'], inp['v'], True, s)\n"
+        "dq, dk, dv = C.attn_cpu_bwd(inp['q'], inp['k'], inp['v'], o, inp['do'], lse, True, s)\n"
+        "np.savez(sys.argv[1], o=o, lse=lse, dq=dq, dk=dk, dv=dv)\n"
+    )
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    import tempfile
+
+    with tempfile.TemporaryDirectory() as tmp:
+        out = os.path.join(tmp, "avx2.npz")
+        env = dict(os.environ, ATTN_CPU_ISA="avx2")
+        r = subprocess.run([sys.executable, "-c", code, out], cwd=root, env=env, capture_output=True, text=True,
+                           timeout=300)
+        assert r.returncode == 0, r.stderr[-2000:]
+        ref = np.load(out)
+        for name, got in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+            assert np.array_equal(got, ref[name]), name
