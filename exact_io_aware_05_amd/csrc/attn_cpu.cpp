@@ -19,6 +19,7 @@
 // multiply-add each, so both forms give the same results.
 #include "attn_cpu.h"
 
+#include <immintrin.h>
 #include <omp.h>
 
 #include <algorithm>
@@ -60,6 +61,27 @@ inline float exp2_sm(float x) {
   const uint32_t bits = (uint32_t)e << 23;
   std::memcpy(&s, &bits, 4);
   return p * s;
+}
+
+// exp2_sm on eight values at once: the same operations per element (clamps,
+// rounding, polynomial, exponent field), so each lane equals exp2_sm of it.
+inline v8f exp2_v8(v8f x) {
+  const v8f lo = v8f{} - 127.f, hi = v8f{} + 127.f;
+  x = x < lo ? lo : x;
+  x = x > hi ? hi : x;
+  const v8f n = (v8f)_mm256_floor_ps((__m256)(x + 0.5f));
+  const v8f f = x - n;
+  v8f p = v8f{} + 1.5252733804059838e-05f;
+  p = p * f + 1.5403530393381606e-04f;
+  p = p * f + 1.3333558146428441e-03f;
+  p = p * f + 9.6181291076284770e-03f;
+  p = p * f + 5.5504108664821576e-02f;
+  p = p * f + 2.4022650695910071e-01f;
+  p = p * f + 6.9314718055994531e-01f;
+  p = p * f + 1.0f;
+  const __m256i e = _mm256_add_epi32(_mm256_cvttps_epi32((__m256)n), _mm256_set1_epi32(127));
+  const v8f sc = (v8f)_mm256_castsi256_ps(_mm256_slli_epi32(e, 23));
+  return p * sc;
 }
 
 // Rows i0 .. i0 + RB - 1 of C, columns c0 .. c0 + NV * lanes(V) - 1:
@@ -225,18 +247,33 @@ extern "C" int attn_cpu_fwd(const float* q, const float* k, const float* v, floa
         for (int i = 0; i < rows; ++i) {
           float* s = &S[(size_t)i * BK];
           const int lim = causal ? std::min(kend, q0 + i + 1) : n;  // keys [j0, lim) are visible
-          float mx = m[i];
-          for (int j = 0; j < BK; ++j) {
-            s[j] = j0 + j < lim ? s[j] * c : -INFINITY;
-            mx = std::max(mx, s[j]);
+          // Eight lanes at a time (BK = 64): scaled scores with the hidden
+          // keys at -inf, their max, then the exponentials and their sum (as
+          // eight partial sums).
+          typedef int v8i __attribute__((vector_size(32)));
+          const v8i lane = {0, 1, 2, 3, 4, 5, 6, 7};
+          const v8f ninf = v8f{} - INFINITY;
+          v8f mxv = v8f{} + m[i];
+          for (int j = 0; j < BK; j += 8) {
+            v8f x;
+            std::memcpy(&x, s + j, 32);
+            x = (lane + (j0 + j)) < lim ? x * c : ninf;
+            std::memcpy(s + j, &x, 32);
+            mxv = mxv > x ? mxv : x;
           }
+          float mx = mxv[0];
+          for (int t = 1; t < 8; ++t) mx = std::max(mx, mxv[t]);
           // Row i sees key j0 at least (square causal: j0 <= q0 <= i), so mx is finite.
           const float alpha = exp2_sm(m[i] - mx);
-          float sum = 0.f;
-          for (int j = 0; j < BK; ++j) {
-            s[j] = exp2_sm(s[j] - mx);
-            sum += s[j];
+          v8f sv = v8f{};
+          for (int j = 0; j < BK; j += 8) {
+            v8f x;
+            std::memcpy(&x, s + j, 32);
+            x = exp2_v8(x - mx);
+            std::memcpy(s + j, &x, 32);
+            sv += x;
           }
+          const float sum = ((sv[0] + sv[1]) + (sv[2] + sv[3])) + ((sv[4] + sv[5]) + (sv[6] + sv[7]));
           l[i] = l[i] * alpha + sum;
           m[i] = mx;
           float* a = &acc[(size_t)i * dp];
@@ -294,10 +331,17 @@ extern "C" int attn_cpu_bwd(const float* q, const float* k, const float* v, cons
       const float l2 = live ? L2[(size_t)h * n + r] : 0.f;
       const float dr = live ? Dv[(size_t)h * n + r] : 0.f;
       const int lim = !live ? 0 : (causal ? std::min(n, r + 1) : n);
-      for (int j = 0; j < BK; ++j) {
-        const float p = k0 + j < lim ? exp2_sm(P[i * BK + j] * c - l2) : 0.f;
-        P[i * BK + j] = p;
-        dS[i * BK + j] = p * (dP[i * BK + j] - dr);
+      typedef int v8i __attribute__((vector_size(32)));
+      const v8i lane = {0, 1, 2, 3, 4, 5, 6, 7};
+      for (int j = 0; j < BK; j += 8) {
+        v8f pv, dpv;
+        std::memcpy(&pv, P + i * BK + j, 32);
+        std::memcpy(&dpv, dP + i * BK + j, 32);
+        const v8f e = exp2_v8(pv * c - l2);
+        const v8f pm = (lane + (k0 + j)) < lim ? e : v8f{};
+        const v8f ds = pm * (dpv - dr);
+        std::memcpy(P + i * BK + j, &pm, 32);
+        std::memcpy(dS + i * BK + j, &ds, 32);
       }
     }
   };

@@ -120,6 +120,7 @@ def test_vector_paths_give_identical_results():
         "import sys, math, numpy as np\n"
         "import synth\n"
         "from exact_io_aware_05_amd import cpu as C\n"
+        "C.CPU_LIB_PATH = sys.argv[2]\n"
         "inp = synth.qkvdo(77, (1, 2, 150, 64), 'bf16')\n"
         "s = 1.0 / math.sqrt(64)\n"
         "o, lse = C.attn_cpu_fwd(inp['q'], inp['k'], inp['v'], True, s)\n"
@@ -132,8 +133,9 @@ def test_vector_paths_give_identical_results():
     with tempfile.TemporaryDirectory() as tmp:
         out = os.path.join(tmp, "avx2.npz")
         env = dict(os.environ, ATTN_CPU_ISA="avx2")
-        r = subprocess.run([sys.executable, "-c", code, out], cwd=root, env=env, capture_output=True, text=True,
-                           timeout=300)
+        # The child loads the same library file (the sanitizer run swaps it).
+        r = subprocess.run([sys.executable, "-c", code, out, C.CPU_LIB_PATH], cwd=root, env=env, capture_output=True,
+                           text=True, timeout=300)
         assert r.returncode == 0, r.stderr[-2000:]
         ref = np.load(out)
         for name, got in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
