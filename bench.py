@@ -463,8 +463,8 @@ def probes(torch):
     """Diagnostic microbenchmarks, one JSON line each: fp32 atomic adds of a dQ
     accumulated by key blocks (and plain stores of the same tiles) at the
     B=8 H=16 N=2048 d=64 and B=4 H=16 N=4096 d=128 shapes, the instruction-mix
-    cycles at one and two waves per SIMD, and the MFMA rate and clock under
-    load."""
+    cycles at one and two waves per SIMD, the MFMA rate and clock under load,
+    and the read bandwidth of a plain streaming kernel over 1 GiB."""
     from exact_io_aware_05_amd import diag
 
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -485,6 +485,13 @@ def probes(torch):
     r = diag.mfma_rate(cus)
     print(json.dumps({"probe": "mfma_rate", "cus": cus, "tflops": round(r["tflops"], 1), "ghz": round(r["ghz"], 3),
                       "frac_of_2516.6": round(r["tflops"] / 2516.6, 3)}), flush=True)
+    for wgs_per_cu in (1, 2, 4, 8):
+        for unroll in (4, 8, 16):
+            r = diag.read_bw(1 << 30, wgs_per_cu * cus, unroll)
+            print(json.dumps({"probe": "read_bw", "bytes": 1 << 30, "workgroups": wgs_per_cu * cus,
+                              "loads_in_flight_per_thread": unroll, "ms": round(r["ms"], 4),
+                              "GB_per_s": round(r["GB_per_s"], 1), "frac_of_8000": round(r["GB_per_s"] / 8000, 4)}),
+                  flush=True)
 
 
 def _upload(torch, inp, dtype):

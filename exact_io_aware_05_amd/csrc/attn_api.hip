@@ -84,15 +84,28 @@ struct SplitPlan {
   int kchunk;
 };
 
-SplitPlan split_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int num_splits) {
+// The forward of few query rows over at least as many keys runs the
+// vector-ALU decode kernel.
+bool use_decode(int64_t Nq, int64_t Nk) { return Nq <= attn::decode_max_rows() && Nq <= Nk; }
+
+SplitPlan split_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int num_splits) {
   const int64_t ktiles = (Nk + 63) / 64;
   int64_t want = num_splits;
   if (num_splits == 0) {
-    // Enough workgroups to fill the chip twice over (256 CUs, two per CU),
-    // each chunk at least 4 tiles.
-    const int64_t wgs = B * H * ((Nq + 127) / 128);
-    want = (1024 + wgs - 1) / wgs;
-    want = want < ktiles / 4 ? want : ktiles / 4;
+    if (use_decode(Nq, Nk)) {
+      // Decode kernel: about four workgroups per CU (256 CUs), each chunk at
+      // least one pass of the workgroup's waves.
+      const int64_t wgs = B * H;
+      const int64_t min_tiles = attn::decode_wg_keys(d) / 64;
+      want = (1024 + wgs - 1) / wgs;
+      want = want < ktiles / min_tiles ? want : ktiles / min_tiles;
+    } else {
+      // Enough workgroups to fill the chip twice over (256 CUs, two per CU),
+      // each chunk at least 4 tiles.
+      const int64_t wgs = B * H * ((Nq + 127) / 128);
+      want = (1024 + wgs - 1) / wgs;
+      want = want < ktiles / 4 ? want : ktiles / 4;
+    }
   }
   if (want > 64) want = 64;
   if (want > ktiles) want = ktiles;
@@ -504,7 +517,7 @@ int attn_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
 size_t attn_fwd_qk_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype,
                                    int num_splits) {
   if (check_qk(B, H, Nq, Nk, d, dtype) != ATTN_OK || num_splits < 0 || num_splits > 64) return 0;
-  const SplitPlan sp = split_plan(B, H, Nq, Nk, num_splits);
+  const SplitPlan sp = split_plan(B, H, Nq, Nk, d, num_splits);
   if (sp.nsplit < 2) return 0;
   const size_t rows = (size_t)(B * H * Nq) * (size_t)sp.nsplit;
   return align256(rows * (size_t)d * sizeof(float)) + align256(rows * sizeof(float));
@@ -519,7 +532,7 @@ int attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse
   if (st != ATTN_OK) return st;
   if (num_splits < 0 || num_splits > 64) return ATTN_E_SHAPE;
   if (!isfinite(scale)) return ATTN_E_SCALE;
-  const SplitPlan sp = split_plan(B, H, Nq, Nk, num_splits);
+  const SplitPlan sp = split_plan(B, H, Nq, Nk, d, num_splits);
   const size_t need = attn_fwd_qk_workspace_bytes(B, H, Nq, Nk, d, dtype, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255) != 0))
     return ATTN_E_WORKSPACE;
@@ -543,7 +556,7 @@ int attn_fwd_qk(const void* q, const void* k, const void* v, void* o, float* lse
     a.opart = (float*)workspace;
     a.lpart = (float*)((char*)workspace + align256(rows * (size_t)d * sizeof(float)));
   }
-  if (attn::fwd_bf16(a) != hipSuccess) return ATTN_E_HIP;
+  if ((use_decode(Nq, Nk) ? attn::fwd_decode(a) : attn::fwd_bf16(a)) != hipSuccess) return ATTN_E_HIP;
   if (sp.nsplit > 1 && attn::fwd_combine(a) != hipSuccess) return ATTN_E_HIP;
   return ATTN_OK;
 }

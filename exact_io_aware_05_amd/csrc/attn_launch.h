@@ -144,6 +144,14 @@ constexpr int kSparseBlock = 128;
 hipError_t fwd_bf16(const FwdArgs& a);
 // Merge of the split-K/V partial results into O (bf16) and LSE.
 hipError_t fwd_combine(const FwdArgs& a);
+// Forward for 1 <= n <= decode_max_rows() query rows over nk >= n keys
+// (unequal lengths, no mask other than causal): vector-ALU kernel, split
+// over keys as the matrix-core kernel (same partials, merged by fwd_combine).
+hipError_t fwd_decode(const FwdArgs& a);
+int decode_max_rows();
+// Keys one decode workgroup covers in one pass of its waves (the smallest
+// chunk that keeps every wave busy).
+int decode_wg_keys(int64_t d);
 hipError_t fwd_f32(const FwdArgs& a);
 // Backward phases; `o` is read only by bwd_dsum, `dq` written only by the
 // *_dq launchers, `dk`/`dv` only by the *_dkdv launchers.

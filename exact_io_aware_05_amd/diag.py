@@ -47,7 +47,8 @@ def lib():
         L.probe_atomic_dq.argtypes = [i, i, i, i, i, i, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_longlong)]
         L.probe_issue_mix.argtypes = [i, i, i, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
         L.probe_mfma_rate.argtypes = [i, i, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
-        for f in (L.probe_atomic_dq, L.probe_issue_mix, L.probe_mfma_rate):
+        L.probe_read_bw.argtypes = [ctypes.c_longlong, i, i, i, ctypes.POINTER(ctypes.c_float)]
+        for f in (L.probe_atomic_dq, L.probe_issue_mix, L.probe_mfma_rate, L.probe_read_bw):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -84,3 +85,12 @@ def mfma_rate(num_cus, iters=20000):
     tf, ghz = ctypes.c_double(), ctypes.c_double()
     _check(lib().probe_mfma_rate(num_cus, iters, ctypes.byref(tf), ctypes.byref(ghz)), "probe_mfma_rate")
     return {"tflops": tf.value, "ghz": ghz.value}
+
+
+def read_bw(nbytes, grid, unroll=8, reps=20):
+    """Plain streaming read of ``nbytes`` by ``grid`` workgroups: ms per
+    launch and GB/s."""
+    ms = ctypes.c_float()
+    _check(lib().probe_read_bw(nbytes, grid, unroll, reps, ctypes.byref(ms)), "probe_read_bw")
+    return {"ms": ms.value, "GB_per_s": nbytes / (ms.value * 1e-3) / 1e9}
+

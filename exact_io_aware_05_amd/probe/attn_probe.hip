@@ -12,6 +12,10 @@
 //  * probe_mfma_rate: every SIMD of every CU runs independent MFMAs back to
 //    back; the achieved bf16 rate and the shader clock under that load
 //    (s_memtime cycles over event time).
+//  * probe_read_bw: HBM read bandwidth of a plain streaming kernel -- each
+//    workgroup reads a contiguous share of a buffer in 16-byte loads (1 KiB
+//    per wave instruction, as the decode kernel's), a fixed number in flight
+//    per thread -- for a given grid size.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -175,6 +179,26 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(float* out, long long* c
   if ((threadIdx.x & 63) == 0) cyc[blockIdx.x * 4 + threadIdx.x / 64] = t1 - t0;
 }
 
+// ---------------------------------------------------------------- HBM read
+template <int U>
+__global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ p, long long n16, unsigned* out) {
+  const long long per = (n16 + gridDim.x - 1) / gridDim.x;
+  const long long c0 = (long long)blockIdx.x * per;
+  const long long c1 = c0 + per < n16 ? c0 + per : n16;
+  unsigned x = 0;
+  for (long long i = c0 + threadIdx.x; i < c1; i += 256LL * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const long long idx = i + 256LL * u;
+      v[u] = idx < c1 ? p[idx] : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  out[(size_t)blockIdx.x * 256 + threadIdx.x] = x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -279,6 +303,42 @@ int probe_mfma_rate(int num_cus, int iters, double* tflops, double* ghz) {
   if (b) (void)hipEventDestroy(b);
   (void)hipFree(out);
   (void)hipFree(cyc);
+  return e;
+}
+
+// HBM read bandwidth: `bytes` (a multiple of 16) read by `grid` workgroups
+// of 256 threads, `unroll` (4, 8 or 16) 16-byte loads in flight per thread;
+// the average ms of `reps` launches after one warm-up launch.
+int probe_read_bw(long long bytes, int grid, int unroll, int reps, float* ms) {
+  if (!ms || bytes <= 0 || bytes % 16 || grid <= 0 || reps <= 0) return hipErrorInvalidValue;
+  if (unroll != 4 && unroll != 8 && unroll != 16) return hipErrorInvalidValue;
+  const long long n16 = bytes / 16;
+  uint4* buf = nullptr;
+  unsigned* out = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  hipError_t e = hipMalloc(&buf, (size_t)bytes);
+  if (e == hipSuccess) e = hipMalloc(&out, (size_t)grid * 256 * sizeof(unsigned));
+  if (e == hipSuccess) e = hipMemset(buf, 0x5A, (size_t)bytes);
+  if (e == hipSuccess) e = hipEventCreate(&a);
+  if (e == hipSuccess) e = hipEventCreate(&b);
+  auto launch = [&]() {
+    if (unroll == 4) read_kernel<4><<<grid, 256>>>(buf, n16, out);
+    else if (unroll == 8) read_kernel<8><<<grid, 256>>>(buf, n16, out);
+    else read_kernel<16><<<grid, 256>>>(buf, n16, out);
+    return hipGetLastError();
+  };
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipEventRecord(a);
+  for (int r = 0; r < reps && e == hipSuccess; ++r) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b);
+  if (e == hipSuccess) e = hipEventSynchronize(b);
+  if (e == hipSuccess) e = hipEventElapsedTime(ms, a, b);
+  if (e == hipSuccess) *ms /= reps;
+  if (a) (void)hipEventDestroy(a);
+  if (b) (void)hipEventDestroy(b);
+  (void)hipFree(buf);
+  (void)hipFree(out);
   return e;
 }
 

@@ -256,6 +256,12 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v,
  * form LSE = log sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
  * num_splits = 1: no split (no workspace); 2..64: at most that many chunks
  * (fewer if Nk has fewer tiles); 0: chosen by the library from the shape.
+ * One to four query rows over at least as many keys (decoding) run a
+ * vector-ALU kernel that streams K and V once (the matrix-core kernel's
+ * 128-row tile would be mostly empty); its automatic split aims at about
+ * 1024 workgroups with chunks of at least 128 keys (d = 128) or 256 (d = 64).
+ * More rows: about 1024 workgroups of 128 query rows, chunks of at least
+ * 256 keys.
  *
  *   attn_fwd_qk_workspace_bytes : bytes attn_fwd_qk needs for this shape and
  *                                 num_splits (0 when no split is used, or on

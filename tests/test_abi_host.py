@@ -303,6 +303,33 @@ def test_unequal_lengths_backward_workspace_holds_the_dq_split():
     assert L.attn_bwd_qk_workspace_bytes(1, 1, 1, 7 * 64, 128, 0) == dbytes(1, 1, 1)
 
 
+def test_decode_forward_split_plan():
+    # One to four query rows over at least as many keys take the decode
+    # kernel, whose automatic split aims at about 1024 workgroups with chunks
+    # of at least one pass of its waves (128 keys at d = 128, 256 at d = 64);
+    # more rows keep the matrix-core plan (about 1024 workgroups of 128 rows,
+    # at least 4 tiles a chunk).  Workspace: fp32 O and LSE per row and chunk.
+    _, L = _lib()
+
+    def wsb(B, H, nq, chunks, d):
+        rows = B * H * nq * chunks
+        return -(-(rows * d * 4) // 256) * 256 + -(-(rows * 4) // 256) * 256
+
+    # 8 heads, 79 tiles: at most 128 chunks by workgroups, 39 of 2 tiles -> 27 of 3.
+    assert L.attn_fwd_qk_workspace_bytes(2, 4, 1, 5000, 128, 0, 0) == wsb(2, 4, 1, 27, 128)
+    assert L.attn_fwd_qk_workspace_bytes(2, 4, 4, 5000, 128, 0, 0) == wsb(2, 4, 4, 27, 128)
+    # Five rows: the matrix-core plan, 19 chunks of 4 tiles -> 16 of 5.
+    assert L.attn_fwd_qk_workspace_bytes(2, 4, 5, 5000, 128, 0, 0) == wsb(2, 4, 5, 16, 128)
+    # d = 64: chunks of at least 4 tiles; 32 heads, 64 tiles -> 16 chunks.
+    assert L.attn_fwd_qk_workspace_bytes(1, 32, 1, 4096, 64, 0, 0) == wsb(1, 32, 1, 16, 64)
+    # 32 heads at d = 128 over 4096 keys: 32 chunks of 2 tiles.
+    assert L.attn_fwd_qk_workspace_bytes(1, 32, 1, 4096, 128, 0, 0) == wsb(1, 32, 1, 32, 128)
+    # Enough heads for the chip: no split.
+    assert L.attn_fwd_qk_workspace_bytes(16, 64, 1, 4096, 128, 0, 0) == 0
+    # Explicit counts are honoured as for more rows.
+    assert L.attn_fwd_qk_workspace_bytes(2, 4, 1, 5000, 128, 0, 8) == wsb(2, 4, 1, 8, 128)
+
+
 def test_workspace_size():
     E, L = _lib()
     assert E.attn_bwd_workspace_bytes(2, 3, 100, 64, 0) >= 2 * 3 * 100 * 4

@@ -13,7 +13,7 @@ from exact_io_aware_05_amd import diag
 
 def test_probe_library_exports():
     L = diag.lib()
-    for name in ("probe_atomic_dq", "probe_issue_mix", "probe_mfma_rate"):
+    for name in ("probe_atomic_dq", "probe_issue_mix", "probe_mfma_rate", "probe_read_bw"):
         assert hasattr(L, name), name
 
 
@@ -28,6 +28,9 @@ def test_probe_rejects_bad_sizes_on_the_host():
     assert L.probe_issue_mix(0, 3, 256, ctypes.byref(mean), ctypes.byref(mx)) != 0
     tf, ghz = ctypes.c_double(), ctypes.c_double()
     assert L.probe_mfma_rate(0, 10, ctypes.byref(tf), ctypes.byref(ghz)) != 0
+    assert L.probe_read_bw(1000, 8, 8, 1, ctypes.byref(ms)) != 0  # not a multiple of 16
+    assert L.probe_read_bw(1 << 20, 8, 5, 1, ctypes.byref(ms)) != 0  # unroll
+    assert L.probe_read_bw(1 << 20, 0, 8, 1, ctypes.byref(ms)) != 0  # grid
 
 
 @pytest.fixture(scope="module")
@@ -54,6 +57,8 @@ def test_issue_and_rate_probes(cus):
     assert 400 < r["max_cycles"] < 800
     r = diag.mfma_rate(cus, iters=2000)
     assert r["tflops"] > 0 and 0.5 < r["ghz"] < 4.0
+    r = diag.read_bw(64 << 20, 4 * cus, reps=3)
+    assert r["ms"] > 0 and r["GB_per_s"] < 8000 * 1.05
 
 
 def test_bindings_load_torch_before_their_hip_library():

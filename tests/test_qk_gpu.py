@@ -90,6 +90,145 @@ def test_decode_split_kv(nq, d, causal, splits):
     _check_fwd(download(o), download(lse), o_r, lse_r)
 
 
+DECODE_CASES = [
+    # (B, H, Nq, Nk, d): one to four query rows (the vector-ALU decode kernel)
+    (1, 3, 1, 1, 128),  # a single key
+    (2, 2, 1, 63, 64),  # less than one load batch
+    (1, 2, 2, 2, 128),  # as many queries as keys
+    (2, 3, 3, 129, 128),  # ragged last chunk
+    (1, 2, 4, 4, 64),
+    (2, 2, 4, 1000, 64),
+    (1, 4, 3, 4097, 128),
+]
+
+
+@pytest.mark.parametrize("splits", [1, 2, 0])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", DECODE_CASES)
+def test_decode_kernel_rows_and_tails(case, causal, splits):
+    E = _api()
+    B, H, nq, nk, d = case
+    seed = 6300 + 7 * nq + nk + d + causal
+    _announce("decode kernel", case, "causal" if causal else "full", "splits", splits, "seed", seed)
+    inp = _inputs(seed, B, H, nq, nk, d)
+    q, k, v = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v"))
+    o, lse = E.attn_fwd_qk(q, k, v, causal=causal, num_splits=splits)
+    torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], causal)
+    _check_fwd(download(o), download(lse), o_r, lse_r)
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.02])
+def test_decode_kernel_scales(scale):
+    # Negative and small scales (the kernel multiplies the fp32 score by
+    # scale * log2(e) before the max).
+    E = _api()
+    B, H, nq, nk, d = 2, 2, 2, 777, 128
+    _announce("decode kernel scale", scale)
+    inp = _inputs(6400, B, H, nq, nk, d)
+    q, k, v = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v"))
+    o, lse = E.attn_fwd_qk(q, k, v, causal=True, scale=scale, num_splits=0)
+    torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], True, scale)
+    _check_fwd(download(o), download(lse), o_r, lse_r)
+
+
+def test_decode_kernel_many_heads_unsplit():
+    # 1024 heads fill the chip without a split: every workgroup writes O and
+    # LSE directly.
+    E = _api()
+    B, H, nq, nk, d = 16, 64, 1, 300, 64
+    _announce("decode kernel many heads", (B, H, nq, nk, d))
+    assert E.lib().attn_fwd_qk_workspace_bytes(B, H, nq, nk, d, E.ATTN_BF16, 0) == 0
+    inp = _inputs(6500, B, H, nq, nk, d)
+    q, k, v = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v"))
+    o, lse = E.attn_fwd_qk(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], False)
+    _check_fwd(download(o), download(lse), o_r, lse_r)
+
+
+def _decode_setup(E, B, H, nq, nk, d, seed):
+    inp = _inputs(seed, B, H, nq, nk, d)
+    q, k, v = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v"))
+    need = int(E.lib().attn_fwd_qk_workspace_bytes(B, H, nq, nk, d, E.ATTN_BF16, 0))
+    assert need > 0
+    return inp, q, k, v, need
+
+
+def test_decode_kernel_deterministic():
+    # The chunks' partials are merged in a fixed order: the result does not
+    # depend on the workspace's earlier contents, and repeated calls give the
+    # first call's bits.
+    E = _api()
+    B, H, nq, nk, d = 2, 3, 1, 3000, 128
+    _announce("decode kernel determinism", (B, H, nq, nk, d))
+    inp, q, k, v, need = _decode_setup(E, B, H, nq, nk, d, 6600)
+    zero = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    o0, l0 = E.attn_fwd_qk(q, k, v, causal=True, num_splits=0, workspace=zero)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    noise = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=g)
+    ones = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    for name, ws in (("random", noise), ("ones", ones)):
+        o, l = E.attn_fwd_qk(q, k, v, causal=True, num_splits=0, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o0) and torch.equal(l, l0), name
+    outs = [E.attn_fwd_qk(q, k, v, causal=True, num_splits=0, workspace=zero) for _ in range(40)]
+    torch.cuda.synchronize()
+    for i, (o, l) in enumerate(outs):
+        assert torch.equal(o, o0) and torch.equal(l, l0), f"call {i}"
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], True)
+    _check_fwd(download(o0), download(l0), o_r, lse_r)
+
+
+def test_decode_kernel_many_heads_split_merged_separately():
+    # More than 1024 heads with an explicit split (the automatic plan would
+    # not split): 2080 workgroups of two chunks each.
+    E = _api()
+    B, H, nq, nk, d = 2, 520, 1, 600, 64
+    _announce("decode kernel many heads split", (B, H, nq, nk, d))
+    inp = _inputs(6800, B, H, nq, nk, d)
+    q, k, v = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v"))
+    o, lse = E.attn_fwd_qk(q, k, v, causal=False, num_splits=2)
+    torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], False)
+    _check_fwd(download(o), download(lse), o_r, lse_r)
+
+
+def test_decode_kernel_graph_replays():
+    # The decode kernel and the merge kernel captured once and replayed, with
+    # eager calls on another workspace between the replays.
+    E = _api()
+    B, H, nq, nk, d = 1, 4, 2, 2500, 64
+    _announce("decode kernel graph", (B, H, nq, nk, d))
+    inp, q, k, v, need = _decode_setup(E, B, H, nq, nk, d, 6700)
+    ws_e = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ref_o, ref_l = E.attn_fwd_qk(q, k, v, causal=True, num_splits=0, workspace=ws_e)
+    torch.cuda.synchronize()
+    ws_g = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, nq), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        E.attn_fwd_qk(q, k, v, causal=True, num_splits=0, out=o, lse=lse, workspace=ws_g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        E.attn_fwd_qk(q, k, v, causal=True, num_splits=0, out=o, lse=lse, workspace=ws_g)
+    for i in range(4):
+        o.zero_()
+        lse.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l), f"replay {i}"
+        E.attn_fwd_qk(q, k, v, causal=True, num_splits=0, workspace=ws_e)
+        torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], True)
+    _check_fwd(download(ref_o), download(ref_l), o_r, lse_r)
+
+
 def test_long_decode_auto_split():
     # Four queries after 65532 cached tokens, one head group, automatic split.
     E = _api()
