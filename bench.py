@@ -655,6 +655,27 @@ def _time_ms(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def _time_graph_ms(torch, fn, steps, warmup):
+    """Per-call time of `steps` calls captured in one HIP graph and replayed
+    (no host work between the calls): for calls short enough that Python's
+    own per-call overhead would otherwise leave the GPU idle between them."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def dropout(torch, E, steps, warmup):
     """Fused dropout against the plain path at B=4 H=16 N=4096 d=128, bf16:
     forward and whole backward (D, dK/dV, dQ) per mask, p = 0.1, TFLOP/s by
@@ -725,11 +746,26 @@ def window(torch, E, steps, warmup):
         torch.cuda.empty_cache()
 
 
+def _decode_line(torch, call, steps, warmup, b, h, nq, nk, d, kv_bytes, splits):
+    """One decode JSON line: the per-call time of back-to-back eager calls
+    (`eager_ms`, which includes the Python binding's per-call host work when
+    that exceeds the GPU time) and of the same calls replayed from a HIP graph
+    (`ms`, GPU time); rates from the latter."""
+    eager = _time_ms(torch, call, steps, warmup)
+    ms = _time_graph_ms(torch, call, steps, warmup)
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    return {"decode": True, "B": b, "H": h, "Nq": nq, "Nk": nk, "d": d, "causal": True, "num_splits": splits,
+            "ms": round(ms, 4), "eager_ms": round(eager, 4), "kv_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def decode(torch, E, steps, warmup):
     """Unequal lengths.  Decoding: one query per head after Nk cached tokens
     (B=1, H=32, d=128, causal bottom-right), HBM-bound: reported as the K and V
     bytes read per second against 8 TB/s, with one pass and with the
-    library's split-K/V choice.  Chunked prefill: 1024 queries after 7168
+    library's split-K/V choice; then four query rows (d=128) and one at d=64
+    over 16384 keys.  Each decode line gives the eager per-call time and the
+    time of the same calls replayed from a HIP graph (rates from the latter).  Chunked prefill: 1024 queries after 7168
     cached tokens (B=1, H=16, d=128, causal): TFLOP/s over the allowed pairs,
     forward (library's split choice) and backward."""
     g = torch.Generator(device="cuda").manual_seed(13)
@@ -738,17 +774,27 @@ def decode(torch, E, steps, warmup):
         q = torch.randn(b, h, 1, d, device="cuda", generator=g).to(torch.bfloat16)
         k, v = (torch.randn(b, h, nk, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
         kv_bytes = 2.0 * b * h * nk * d * 2
+        o = torch.empty_like(q)
+        lse = torch.empty((b, h, 1), dtype=torch.float32, device="cuda")
         for splits in (1, 0):
             nsplit_bytes = E.lib().attn_fwd_qk_workspace_bytes(b, h, 1, nk, d, E.ATTN_BF16, splits)
             ws = torch.empty(max(nsplit_bytes, 256), dtype=torch.uint8, device="cuda")
-            ms = _time_ms(torch, lambda: E.attn_fwd_qk(q, k, v, causal=True, num_splits=splits, workspace=ws),
-                          steps, warmup)
-            gbs = kv_bytes / (ms * 1e-3) / 1e9
-            print(json.dumps({
-                "decode": True, "B": b, "H": h, "Nq": 1, "Nk": nk, "d": d, "causal": True,
-                "num_splits": "auto" if splits == 0 else splits, "ms": round(ms, 4),
-                "kv_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-            }), flush=True)
+            call = lambda: E.attn_fwd_qk(q, k, v, causal=True, num_splits=splits, out=o, lse=lse, workspace=ws)
+            print(json.dumps(_decode_line(torch, call, steps, warmup, b, h, 1, nk, d, kv_bytes,
+                                          "auto" if splits == 0 else splits)), flush=True)
+    # The decode kernel's other variants at Nk = 16384: four query rows (as in
+    # speculative decoding) and d = 64.
+    for nq, dd in ((4, 128), (1, 64)):
+        nk = 16384
+        q = torch.randn(b, h, nq, dd, device="cuda", generator=g).to(torch.bfloat16)
+        k, v = (torch.randn(b, h, nk, dd, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
+        kv_bytes = 2.0 * b * h * nk * dd * 2
+        ws = torch.empty(max(E.lib().attn_fwd_qk_workspace_bytes(b, h, nq, nk, dd, E.ATTN_BF16, 0), 256),
+                         dtype=torch.uint8, device="cuda")
+        o = torch.empty_like(q)
+        lse = torch.empty((b, h, nq), dtype=torch.float32, device="cuda")
+        call = lambda: E.attn_fwd_qk(q, k, v, causal=True, num_splits=0, out=o, lse=lse, workspace=ws)
+        print(json.dumps(_decode_line(torch, call, steps, warmup, b, h, nq, nk, dd, kv_bytes, "auto")), flush=True)
     b, h, nq, nk = 1, 16, 1024, 8192
     q, do = (torch.randn(b, h, nq, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))
     k, v = (torch.randn(b, h, nk, d, device="cuda", generator=g).to(torch.bfloat16) for _ in range(2))

@@ -99,6 +99,7 @@ DECODE_CASES = [
     (1, 2, 4, 4, 64),
     (2, 2, 4, 1000, 64),
     (1, 4, 3, 4097, 128),
+    (1, 2, 4, 3, 64),  # more query rows than keys: the matrix-core kernel (empty first row)
 ]
 
 
