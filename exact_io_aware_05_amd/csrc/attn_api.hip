@@ -100,10 +100,13 @@ SplitPlan split_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, in
       want = (1024 + wgs - 1) / wgs;
       want = want < ktiles / min_tiles ? want : ktiles / min_tiles;
     } else {
-      // Enough workgroups to fill the chip twice over (256 CUs, two per CU),
-      // each chunk at least 4 tiles.
+      // Matrix-core kernel: about 512 workgroups (two resident per CU over
+      // 256 CUs, one round), each chunk at least 4 tiles.  Twice that many
+      // was 10-27% slower on prefill shapes (B=1 H=16 1024 queries after
+      // 7168 keys: 107 against 78 us): more chunks mostly add fp32
+      // partials to write and merge.
       const int64_t wgs = B * H * ((Nq + 127) / 128);
-      want = (1024 + wgs - 1) / wgs;
+      want = (512 + wgs - 1) / wgs;
       want = want < ktiles / 4 ? want : ktiles / 4;
     }
   }

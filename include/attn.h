@@ -260,7 +260,7 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v,
  * vector-ALU kernel that streams K and V once (the matrix-core kernel's
  * 128-row tile would be mostly empty); its automatic split aims at about
  * 1024 workgroups with chunks of at least 128 keys (d = 128) or 256 (d = 64).
- * More rows: about 1024 workgroups of 128 query rows, chunks of at least
+ * More rows: about 512 workgroups of 128 query rows, chunks of at least
  * 256 keys.
  *
  *   attn_fwd_qk_workspace_bytes : bytes attn_fwd_qk needs for this shape and

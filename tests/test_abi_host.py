@@ -307,7 +307,7 @@ def test_decode_forward_split_plan():
     # One to four query rows over at least as many keys take the decode
     # kernel, whose automatic split aims at about 1024 workgroups with chunks
     # of at least one pass of its waves (128 keys at d = 128, 256 at d = 64);
-    # more rows keep the matrix-core plan (about 1024 workgroups of 128 rows,
+    # more rows keep the matrix-core plan (about 512 workgroups of 128 rows,
     # at least 4 tiles a chunk).  Workspace: fp32 O and LSE per row and chunk.
     _, L = _lib()
 
@@ -326,6 +326,11 @@ def test_decode_forward_split_plan():
     assert L.attn_fwd_qk_workspace_bytes(1, 32, 1, 4096, 128, 0, 0) == wsb(1, 32, 1, 32, 128)
     # Enough heads for the chip: no split.
     assert L.attn_fwd_qk_workspace_bytes(16, 64, 1, 4096, 128, 0, 0) == 0
+    # Chunked prefill, 1024 queries after 7168 keys, 16 heads: 128 workgroups
+    # of 128 rows -> 4 chunks of 32 tiles (about 512 workgroups).
+    assert L.attn_fwd_qk_workspace_bytes(1, 16, 1024, 8192, 128, 0, 0) == wsb(1, 16, 1024, 4, 128)
+    # 512 workgroups already: no split.
+    assert L.attn_fwd_qk_workspace_bytes(4, 16, 1024, 8192, 128, 0, 0) == 0
     # Explicit counts are honoured as for more rows.
     assert L.attn_fwd_qk_workspace_bytes(2, 4, 1, 5000, 128, 0, 8) == wsb(2, 4, 1, 8, 128)
 
