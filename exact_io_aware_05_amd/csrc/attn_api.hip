@@ -120,13 +120,15 @@ SplitPlan split_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, in
 }
 
 // Split of the backward's dQ pass over keys (unequal lengths): with few
-// (head, query block) workgroups, enough chunks to give the chip about two
-// workgroups per CU (256 CUs), each chunk at least 4 tiles.
+// (head, query block) workgroups, enough chunks for about 256 workgroups (one
+// per CU), each chunk at least 4 tiles.  Targets of 512 and 1024 were 2-5%
+// and 10-12% slower on prefill shapes (fp32 partials to write and merge),
+// 128 was 10-20% slower.
 SplitPlan dq_split_plan(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
   const int64_t ktiles = (Nk + 63) / 64;
   const int64_t rows = attn::bwd_dq_rows(d);
   const int64_t wgs = B * H * ((Nq + rows - 1) / rows);
-  int64_t want = (512 + wgs - 1) / wgs;
+  int64_t want = (256 + wgs - 1) / wgs;
   want = want < ktiles / 4 ? want : ktiles / 4;
   if (want > 64) want = 64;
   if (want < 2) return SplitPlan{1, (int)(ktiles * 64)};

@@ -269,10 +269,10 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v,
  *   attn_bwd_qk_workspace_bytes : bytes attn_bwd_qk needs: D ([B, H, Nq]
  *                                 fp32), then, when the shape has few query
  *                                 blocks for the chip (B * H * ceil(Nq / 256)
- *                                 at d = 128, ceil(Nq / 128) at d = 64, well
- *                                 under 512) and at least 8 key tiles, the dQ
+ *                                 at d = 128, ceil(Nq / 128) at d = 64, at
+ *                                 most 128) and at least 8 key tiles, the dQ
  *                                 pass is split over chunks of whole 64-key
- *                                 tiles (about 512 workgroups, at least 4
+ *                                 tiles (about 256 workgroups, at least 4
  *                                 tiles a chunk, at most 64 chunks) and the
  *                                 workspace also holds one fp32 partial dQ
  *                                 [B, H, Nq, d] per chunk; the chunks are

@@ -284,21 +284,22 @@ def test_unequal_lengths_validation_and_workspace():
 def test_unequal_lengths_backward_workspace_holds_the_dq_split():
     # With few (head, query block) workgroups (256 query rows each at d = 128,
     # 128 at d = 64) the dQ pass is split over chunks of whole 64-key tiles,
-    # about 512 workgroups in all and at least 4 tiles a chunk; the workspace
+    # about 256 workgroups in all and at least 4 tiles a chunk; the workspace
     # adds one fp32 [B, H, Nq, d] partial per chunk after D.
     _, L = _lib()
 
     def dbytes(B, H, nq):
         return -(-(B * H * nq * 4) // 256) * 256
 
-    # Chunked prefill: 64 workgroups, 128 tiles -> 8 chunks of 16 tiles.
-    assert L.attn_bwd_qk_workspace_bytes(1, 16, 1024, 8192, 128, 0) == dbytes(1, 16, 1024) + 8 * 16 * 1024 * 128 * 4
+    # Chunked prefill: 64 workgroups, 128 tiles -> 4 chunks of 32 tiles.
+    assert L.attn_bwd_qk_workspace_bytes(1, 16, 1024, 8192, 128, 0) == dbytes(1, 16, 1024) + 4 * 16 * 1024 * 128 * 4
     # Decoding: 8 workgroups, 79 tiles -> at most 19 chunks of 5 tiles -> 16.
     assert L.attn_bwd_qk_workspace_bytes(2, 4, 1, 5000, 128, 0) == dbytes(2, 4, 1) + 16 * 8 * 1 * 128 * 4
     # d = 64: 4 workgroups, 64 tiles -> 16 chunks of 4 tiles.
     assert L.attn_bwd_qk_workspace_bytes(2, 2, 64, 4096, 64, 0) == dbytes(2, 2, 64) + 16 * 4 * 64 * 64 * 4
-    # Enough workgroups already (1024): no split, D only.
+    # Enough workgroups already (1024; 256 too): no split, D only.
     assert L.attn_bwd_qk_workspace_bytes(4, 16, 4096, 8192, 128, 0) == dbytes(4, 16, 4096)
+    assert L.attn_bwd_qk_workspace_bytes(1, 16, 4096, 8192, 128, 0) == dbytes(1, 16, 4096)
     # Fewer than 8 key tiles: no chunk of 4 tiles to split off.
     assert L.attn_bwd_qk_workspace_bytes(1, 1, 1, 7 * 64, 128, 0) == dbytes(1, 1, 1)
 

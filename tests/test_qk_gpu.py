@@ -309,12 +309,12 @@ def test_backward_with_dq_split_over_keys(case, causal):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_chunked_prefill_backward_sampled_heads(causal):
-    # 1024 queries after 7168 cached tokens, 16 heads, d = 128: eight key
-    # chunks of 1024.  Two heads against the oracle, whole.
+    # 1024 queries after 7168 cached tokens, 16 heads, d = 128: the dQ pass in
+    # four key chunks of 2048.  Two heads against the oracle, whole.
     E = _api()
     B, H, nq, nk, d = 1, 16, 1024, 8192, 128
     assert E.lib().attn_bwd_qk_workspace_bytes(B, H, nq, nk, d, E.ATTN_BF16) == (
-        _dsum_bytes(B, H, nq) + 8 * B * H * nq * d * 4)
+        _dsum_bytes(B, H, nq) + 4 * B * H * nq * d * 4)
     _announce("chunked prefill bwd", (B, H, nq, nk, d), "causal" if causal else "full")
     inp = _inputs(6500 + causal, B, H, nq, nk, d)
     q, k, v, do = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v", "do"))
