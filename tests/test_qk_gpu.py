@@ -230,6 +230,34 @@ def test_decode_kernel_graph_replays():
     _check_fwd(download(ref_o), download(ref_l), o_r, lse_r)
 
 
+BENCH_DECODE = [
+    # The benchmark's decode lines (causal, B=1 H=32): one query row over 4096,
+    # 16384 and 65536 keys at d = 128, four rows over 16384, one at d = 64.
+    (1, 32, 1, 4096, 128),
+    (1, 32, 1, 16384, 128),
+    (1, 32, 1, 65536, 128),
+    (1, 32, 4, 16384, 128),
+    (1, 32, 1, 16384, 64),
+]
+
+
+@pytest.mark.parametrize("case", BENCH_DECODE)
+def test_decode_bench_shapes_every_output(case):
+    # Every output row of each benchmark decode shape, in the launch
+    # configurations the benchmark times (the automatic split and one pass).
+    E = _api()
+    B, H, nq, nk, d = case
+    seed = 6900 + nq + d + nk // 1024
+    _announce("decode bench shape", case, "seed", seed)
+    inp = _inputs(seed, B, H, nq, nk, d)
+    q, k, v = (upload(inp[x + "_raw"], "bf16") for x in ("q", "k", "v"))
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], True)
+    for splits in (0, 1):
+        o, lse = E.attn_fwd_qk(q, k, v, causal=True, num_splits=splits)
+        torch.cuda.synchronize()
+        _check_fwd(download(o), download(lse), o_r, lse_r)
+
+
 def test_long_decode_auto_split():
     # Four queries after 65532 cached tokens, one head group, automatic split.
     E = _api()
