@@ -9,7 +9,7 @@
 //  * A group of d / 8 lanes holds one key row, 16 bytes (8 bf16) per lane, so
 //    one load instruction of a wave fetches 64 / (d / 8) consecutive key rows,
 //    1 KiB of contiguous memory.  A wave takes 8 such loads of K and 8 of V
-//    per batch (32 keys at d = 128, 64 at d = 64).
+//    per batch (32 keys at d = 128, 64 at d = 64; 4 of each with four rows).
 //  * The score q . k_j is four v_dot2 (bf16 pairs into fp32) per lane, then a
 //    sum over the group's lanes by DPP adds (quad swaps and row mirrors).
 //  * Every lane group keeps its own softmax state for the keys it holds --
@@ -64,14 +64,14 @@ __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& b, float acc)
 
 // G: query rows per workgroup (nq <= G).  Q, O: [bh, nq, D]; K, V: [bh, nk, D];
 // LSE: [bh, nq].  Chunk s covers keys [s * kchunk, min(nk, (s + 1) * kchunk)).
-template <int D, int G>
+template <int D, int G, int NL = kDecLoads>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, float* __restrict__ opart, float* __restrict__ lpart,
     int nq, int nk, long long coff, int kchunk, int nsplit, float c) {
   constexpr int LPK = D / 8;                // lanes per key row
   constexpr int KPI = 64 / LPK;             // key rows per load instruction
-  constexpr int KB = kDecLoads * KPI;       // keys per wave batch
+  constexpr int KB = NL * KPI;              // keys per wave batch
   constexpr int NG = kDecWaves * KPI;       // lane groups per workgroup
   __shared__ float st_o[G][NG][D];
   __shared__ float st_m[G][NG], st_l[G][NG];
@@ -101,23 +101,23 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(
   }
 
   for (int kb = k0 + w * KB; kb < k1; kb += kDecWaves * KB) {
-    u32x4 kr[kDecLoads], vr[kDecLoads];
+    u32x4 kr[NL], vr[NL];
 #pragma unroll
-    for (int t = 0; t < kDecLoads; ++t) {
+    for (int t = 0; t < NL; ++t) {
       const int key = kb + t * KPI + g;
       kr[t] = key < k1 ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * D) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int t = 0; t < kDecLoads; ++t) {
+    for (int t = 0; t < NL; ++t) {
       const int key = kb + t * KPI + g;
       vr[t] = key < k1 ? *reinterpret_cast<const u32x4*>(Vh + (size_t)key * D) : u32x4{0, 0, 0, 0};
     }
-    float p[G][kDecLoads];
+    float p[G][NL];
 #pragma unroll
     for (int r = 0; r < G; ++r) {
       float mx = m[r];
 #pragma unroll
-      for (int t = 0; t < kDecLoads; ++t) {
+      for (int t = 0; t < NL; ++t) {
         const int key = kb + t * KPI + g;
         const float sc = group_sum<LPK>(dot8(q[r], kr[t], 0.f)) * c;
         p[r][t] = key <= lim[r] ? sc : -INFINITY;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(
       const float corr = fast_exp2(m[r] - ms);
       float sum = 0.f;
 #pragma unroll
-      for (int t = 0; t < kDecLoads; ++t) {
+      for (int t = 0; t < NL; ++t) {
         p[r][t] = fast_exp2(p[r][t] - ms);
         sum += p[r][t];
       }
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(
       for (int e = 0; e < 8; ++e) acc[r][e] *= corr;
     }
 #pragma unroll
-    for (int t = 0; t < kDecLoads; ++t) {
+    for (int t = 0; t < NL; ++t) {
       float vf[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -194,12 +194,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_kernel(
   }
 }
 
-template <int D, int G>
+template <int D, int G, int NL = kDecLoads>
 static hipError_t launch_decode(const FwdArgs& a) {
   const int nsplit = a.nsplit;
   const int kchunk = nsplit > 1 ? a.kchunk : (int)a.nk;
   const long long coff = a.causal ? a.nk - a.n : (long long)a.nk;
-  hipLaunchKernelGGL((decode_kernel<D, G>), dim3((unsigned)(nsplit * a.bh)), dim3(kDecWaves * 64), 0,
+  hipLaunchKernelGGL((decode_kernel<D, G, NL>), dim3((unsigned)(nsplit * a.bh)), dim3(kDecWaves * 64), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                      a.lse, a.opart, a.lpart, (int)a.n, (int)a.nk, coff, kchunk, nsplit, a.scale * kLog2e);
   return hipGetLastError();
@@ -209,7 +209,10 @@ template <int D>
 static hipError_t decode_d(const FwdArgs& a) {
   if (a.n == 1) return launch_decode<D, 1>(a);
   if (a.n == 2) return launch_decode<D, 2>(a);
-  return launch_decode<D, 4>(a);
+  // Four rows hold four output accumulators per lane: half as many loads per
+  // batch keep the kernel at 126 VGPRs (four waves per SIMD instead of three;
+  // 2-3% faster over 16384 keys, the same over 4096 and 65536).
+  return launch_decode<D, 4, kDecLoads / 2>(a);
 }
 
 }  // namespace
