@@ -336,9 +336,10 @@ def test_backward_with_dq_split_over_keys(case, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_chunked_prefill_backward_sampled_heads(causal):
-    # 1024 queries after 7168 cached tokens, 16 heads, d = 128: the dQ pass in
-    # four key chunks of 2048.  Two heads against the oracle, whole.
+def test_chunked_prefill_forward_and_sampled_backward(causal):
+    # 1024 queries after 7168 cached tokens, 16 heads, d = 128: the forward
+    # (four key chunks) on every head, the backward (the dQ pass in four key
+    # chunks of 2048) on four whole heads, against the oracle.
     E = _api()
     B, H, nq, nk, d = 1, 16, 1024, 8192, 128
     assert E.lib().attn_bwd_qk_workspace_bytes(B, H, nq, nk, d, E.ATTN_BF16) == (
@@ -350,8 +351,10 @@ def test_chunked_prefill_backward_sampled_heads(causal):
     o, lse = E.attn_fwd_qk(q, k, v, causal=causal, scale=scale, num_splits=0)
     dq, dk, dv = E.attn_bwd_qk(q, k, v, o, do, lse, causal=causal, scale=scale)
     torch.cuda.synchronize()
+    o_r, lse_r = VL.forward_qk_batched(inp["q"], inp["k"], inp["v"], causal, scale)
+    _check_fwd(download(o), download(lse), o_r, lse_r)
     got = [download(t) for t in (dq, dk, dv)]
-    for h in synth.sample_pairs(6510 + causal, H, 1, 2)[:, 0]:
+    for h in synth.sample_pairs(6510 + causal, H, 1, 4)[:, 0]:
         g_r = VL.backward_qk(inp["q"][0, h], inp["k"][0, h], inp["v"][0, h], inp["do"][0, h], causal, scale)
         for name, g, r in zip(("dQ", "dK", "dV"), got, g_r):
             assert_close(g[0, h], r, "bf16", f"{name} (head {h})")
