@@ -517,11 +517,16 @@ static hipError_t fwd_bf16_t(const FwdArgs& a) {
     return a.causal ? launch_fwd<64, 4, true, SPARSE, QK>(a) : launch_fwd<64, 4, false, SPARSE, QK>(a);
   // d = 128, dense: eight waves (256 query rows) share each K/V tile, which
   // halves the fetch's LDS writes per query (3.3% faster at N = 4096; at
-  // d = 64 eight waves are 6% slower).  Block-sparse workgroups stay one
-  // 128-row mask block; unequal lengths keep four waves.
-  if constexpr (!SPARSE && !QK)
+  // d = 64 eight waves are 6% slower).  Up to N = 2048 four-wave workgroups,
+  // two per CU, overlap one another's start-up and epilogue, which weigh
+  // more against short key loops (N = 1024 causal 8%, N = 2048 causal 2%
+  // faster; from N = 4096 on eight waves are 1.5-2% faster).  Block-sparse
+  // workgroups stay one 128-row mask block; unequal lengths keep four waves.
+  if constexpr (!SPARSE && !QK) {
+    if (a.n <= 2048)
+      return a.causal ? launch_fwd<128, 4, true, false, false>(a) : launch_fwd<128, 4, false, false, false>(a);
     return a.causal ? launch_fwd<128, 8, true, false, false>(a) : launch_fwd<128, 8, false, false, false>(a);
-  else
+  } else
     return a.causal ? launch_fwd<128, 4, true, SPARSE, QK>(a) : launch_fwd<128, 4, false, SPARSE, QK>(a);
 }
 
