@@ -1073,14 +1073,8 @@ hipError_t launch_dkdv(const BwdArgs& a) {
 #define ATTN_DQ_NW128 8  // waves per dQ workgroup at d = 128 (tuning knob)
 #endif
 
-template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false, bool WIN = false>
-hipError_t launch_dq(const BwdArgs& a) {
-  // Block-sparse: one mask block row per workgroup (4 waves), so that every
-  // wave of a workgroup wants every tile the workgroup fetches.  Sliding
-  // window: 4 waves too (the workgroup visits the union of its rows'
-  // windows; at N = 16384, windows of 128-2048 keys, the backward runs 2-7%
-  // faster than with 8).
-  constexpr int NW = (D == 128 && !SPARSE && !WIN) ? ATTN_DQ_NW128 : 4;
+template <int D, int NW, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false, bool WIN = false>
+hipError_t launch_dq_nw(const BwdArgs& a) {
   const int n = (int)a.n;
   const int nqb = (n + NW * 32 - 1) / (NW * 32);
   const int total = (int)(a.bh * nqb);
@@ -1104,6 +1098,26 @@ hipError_t launch_dq(const BwdArgs& a) {
   hipLaunchKernelGGL(dq_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, a.stream, (const f32x4*)a.dqpart,
                      (uint16_t*)a.dq, n4, a.nsplit);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool SPARSE, bool QK, bool DROP = false, bool WIN = false>
+hipError_t launch_dq(const BwdArgs& a) {
+  // Block-sparse: one mask block row per workgroup (4 waves), so that every
+  // wave of a workgroup wants every tile the workgroup fetches.  Sliding
+  // window: 4 waves too (the workgroup visits the union of its rows'
+  // windows; at N = 16384, windows of 128-2048 keys, the backward runs 2-7%
+  // faster than with 8).
+  constexpr int NW = (D == 128 && !SPARSE && !WIN) ? ATTN_DQ_NW128 : 4;
+  // Square lengths up to N = 2048 at d = 128: four waves, two workgroups per
+  // CU overlapping one another's start-up and epilogue against short key
+  // loops (N = 1024: 3-5% faster at full mask, 10-12% causal; N = 2048:
+  // 2-4%); from N = 8192 on eight waves are 2-3% faster.  The arithmetic of
+  // a row does not depend on the wave count.  (Dropout keeps eight: its
+  // four-wave form would spill registers.)
+  if constexpr (NW == 8 && !QK && !DROP) {
+    if (a.n <= 2048) return launch_dq_nw<D, 4, CAUSAL, SPARSE, QK, DROP, WIN>(a);
+  }
+  return launch_dq_nw<D, NW, CAUSAL, SPARSE, QK, DROP, WIN>(a);
 }
 
 template <bool SPARSE, bool QK>

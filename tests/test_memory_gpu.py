@@ -45,7 +45,9 @@ def _extra_bytes(n):
     o, lse = E.attn_fwd(q, k, v, causal=True)
     dq, dk, dv = E.attn_bwd(q, k, v, o, do, lse, causal=True)
     torch.cuda.synchronize()
-    peak = torch.cuda.max_memory_allocated() - base
+    # The peak can be no lower than what is still allocated (the outputs); a
+    # peak statistic read below that (seen once, 0 bytes) falls back to it.
+    peak = max(torch.cuda.max_memory_allocated(), torch.cuda.memory_allocated()) - base
     free1, _ = torch.cuda.mem_get_info()
     reserved1 = torch.cuda.memory_reserved()
     tensor_bytes = 4 * B * H * n * D * 2 + B * H * n * 4  # O, dQ, dK, dV (bf16) + LSE (fp32)
