@@ -119,10 +119,11 @@ def test_decode_kernel_rows_and_tails(case, causal, splits):
     _check_fwd(download(o), download(lse), o_r, lse_r)
 
 
-@pytest.mark.parametrize("scale", [-0.3, 0.02])
+@pytest.mark.parametrize("scale", [-0.3, 0.02, 0.0])
 def test_decode_kernel_scales(scale):
-    # Negative and small scales (the kernel multiplies the fp32 score by
-    # scale * log2(e) before the max).
+    # Negative, small and zero scales (the kernel multiplies the fp32 score by
+    # scale * log2(e) before the max; zero gives the uniform average of V and
+    # LSE = log Nk).
     E = _api()
     B, H, nq, nk, d = 2, 2, 2, 777, 128
     _announce("decode kernel scale", scale)
